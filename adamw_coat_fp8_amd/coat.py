@@ -1,0 +1,200 @@
+"""ctypes binding of libcoat_fp8.so (declared in include/coat_fp8.h).
+
+Argument marshalling only: every step of the optimizer runs in the library's
+HIP kernels.  torch tensors are accepted for convenience (their device pointers
+and torch's current HIP stream are passed through); the library never sees a
+torch type.  Importing this module loads the library and fails loudly if it is
+missing: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcoat_fp8.so")
+
+ABI_VERSION = 1
+GROUP_SIZES = (16, 32, 64, 128)
+
+COAT_OK = 0
+COAT_ERR_NULL_POINTER = 1
+COAT_ERR_INVALID_VALUE = 2
+COAT_ERR_GROUP_SIZE = 3
+COAT_ERR_MISALIGNED = 4
+COAT_ERR_HIP = 5
+
+EXPORTED_SYMBOLS = (
+    "coat_adamw_fp8_step", "coat_fp8_expand_quantize", "coat_fp8_dequantize_expand",
+    "coat_e4m3_encode", "coat_e4m3_decode", "coat_status_string",
+    "coat_last_hip_error", "coat_abi_version",
+)
+
+
+class CoatError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class FP8State(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("k", ctypes.c_void_p)]
+
+
+class AdamWTensor(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+                ("m", FP8State), ("v", FP8State), ("n", ctypes.c_int64)]
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64),
+                ("group_size", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c \"import "
+            f"__graft_entry__; __graft_entry__.build()\"` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.coat_adamw_fp8_step.restype = ctypes.c_int
+    lib.coat_adamw_fp8_step.argtypes = [vp, i32, ctypes.POINTER(AdamWHParams), vp]
+    lib.coat_fp8_expand_quantize.restype = ctypes.c_int
+    lib.coat_fp8_expand_quantize.argtypes = [vp, i64, i32, FP8State, vp]
+    lib.coat_fp8_dequantize_expand.restype = ctypes.c_int
+    lib.coat_fp8_dequantize_expand.argtypes = [vp, vp, vp, i64, i32, vp, vp]
+    lib.coat_e4m3_encode.restype = ctypes.c_int
+    lib.coat_e4m3_encode.argtypes = [vp, i64, vp, vp]
+    lib.coat_e4m3_decode.restype = ctypes.c_int
+    lib.coat_e4m3_decode.argtypes = [vp, i64, vp, vp]
+    lib.coat_status_string.restype = ctypes.c_char_p
+    lib.coat_status_string.argtypes = [ctypes.c_int]
+    lib.coat_last_hip_error.restype = ctypes.c_char_p
+    lib.coat_last_hip_error.argtypes = []
+    lib.coat_abi_version.restype = ctypes.c_int32
+    lib.coat_abi_version.argtypes = []
+    if lib.coat_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH}: ABI version {lib.coat_abi_version()}, "
+                          f"binding expects {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.coat_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != COAT_OK:
+        msg = status_string(status)
+        if status == COAT_ERR_HIP:
+            msg += ": " + lib.coat_last_hip_error().decode()
+        raise CoatError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def num_groups(n: int, group_size: int) -> int:
+    return (n + group_size - 1) // group_size
+
+
+@dataclass
+class QuantState:
+    """One FP8 moment on the device: codes uint8[n], scale/k float32[ng]."""
+    codes: torch.Tensor
+    scale: torch.Tensor
+    k: torch.Tensor
+
+    @classmethod
+    def zeros(cls, n: int, group_size: int, device="cuda") -> "QuantState":
+        ng = num_groups(n, group_size)
+        return cls(torch.zeros(n, dtype=torch.uint8, device=device),
+                   torch.zeros(ng, dtype=torch.float32, device=device),
+                   torch.zeros(ng, dtype=torch.float32, device=device))
+
+    def as_c(self) -> FP8State:
+        return FP8State(_ptr(self.codes), _ptr(self.scale), _ptr(self.k))
+
+
+@dataclass
+class ParamSlot:
+    """One tensor of an optimizer shard: FP32 weights, BF16 gradient, m, v."""
+    w: torch.Tensor
+    grad: torch.Tensor
+    m: QuantState
+    v: QuantState
+
+    def as_c(self) -> AdamWTensor:
+        return AdamWTensor(_ptr(self.w), _ptr(self.grad), self.m.as_c(),
+                           self.v.as_c(), self.w.numel())
+
+
+class TensorList:
+    """Marshalled descriptor array for coat_adamw_fp8_step, built once and
+    reused across steps (the pointers stay valid while the tensors live)."""
+
+    def __init__(self, slots: Sequence[ParamSlot]):
+        self.slots = list(slots)
+        self.array = (AdamWTensor * max(1, len(self.slots)))(
+            *[s.as_c() for s in self.slots])
+
+    def __len__(self):
+        return len(self.slots)
+
+
+def adamw_fp8_step(tensors, *, lr: float, beta1: float, beta2: float, eps: float,
+                   weight_decay: float, step: int, group_size: int = 128, stream=None):
+    """One fused FP8 AdamW step over `tensors` (a TensorList or a sequence of
+    ParamSlot).  Enqueued on `stream` (torch's current stream by default)."""
+    tl = tensors if isinstance(tensors, TensorList) else TensorList(tensors)
+    hp = AdamWHParams(lr, beta1, beta2, eps, weight_decay, step, group_size)
+    _check(lib.coat_adamw_fp8_step(ctypes.addressof(tl.array), len(tl),
+                                   ctypes.byref(hp), _stream(stream)))
+
+
+def adamw_fp8_step_raw(array_ptr: Optional[int], num_tensors: int, hp: AdamWHParams,
+                       stream=None) -> int:
+    """Direct call with a caller-built descriptor array; returns the status."""
+    return lib.coat_adamw_fp8_step(array_ptr, num_tensors,
+                                   ctypes.byref(hp) if hp is not None else None,
+                                   _stream(stream))
+
+
+def expand_quantize(x: torch.Tensor, out: QuantState, group_size: int = 128, stream=None):
+    _check(lib.coat_fp8_expand_quantize(_ptr(x), x.numel(), group_size, out.as_c(),
+                                        _stream(stream)))
+
+
+def dequantize_expand(state: QuantState, out: torch.Tensor, group_size: int = 128,
+                      stream=None):
+    _check(lib.coat_fp8_dequantize_expand(
+        _ptr(state.codes), _ptr(state.scale), _ptr(state.k), state.codes.numel(),
+        group_size, _ptr(out), _stream(stream)))
+
+
+def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None):
+    _check(lib.coat_e4m3_encode(_ptr(x), x.numel(), _ptr(codes), _stream(stream)))
+
+
+def e4m3_decode(codes: torch.Tensor, x: torch.Tensor, stream=None):
+    _check(lib.coat_e4m3_decode(_ptr(codes), codes.numel(), _ptr(x), _stream(stream)))

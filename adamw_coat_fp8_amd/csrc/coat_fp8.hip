@@ -1,0 +1,960 @@
+// coat_fp8.hip -- gfx950 kernels and C ABI of COAT's fused FP8 AdamW step
+// with Dynamic Range Expansion.
+//
+// Sources (see include/coat_fp8.h for the full citations):
+//   [P1] COAT paper review (xllm-io.github.io), section 三 核心公式:
+//        quantizer "FP8量化", AdamW "AdamW优化器更新规则", expansion
+//        equations under "动态范围扩展"; section 四 table (fused optimizer
+//        kernel, shard-local dynamic ranges).
+//   [OCP] OFP8 specification, E4M3 (max 448, min normal 2^-6).
+//
+// Execution model.  The step is an element-wise update plus a per-group
+// reduction, bound by HBM bandwidth (about 14 bytes per parameter), so it uses
+// no matrix cores and no LDS.  One 64-lane wavefront owns a "tile" of 1024
+// consecutive elements of one tensor; each lane owns 16 consecutive elements,
+// so a group of G elements lives in G/16 neighbouring lanes and its max /
+// min reductions are 0..3 DPP steps inside registers.  Per lane, every stream
+// moves in 16-byte accesses: w 4 x 16 B, g 2 x 16 B, codes 1 x 16 B each.
+// Waves walk the tiles of all tensors of one launch with a grid stride;
+// tensor descriptors travel in the kernel arguments.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "coat_fp8.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kElemsPerLane = 16;
+constexpr int kTileElems = kWave * kElemsPerLane;  // 1024
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = kWave * kWavesPerBlock;
+constexpr int kMaxTensorsPerLaunch = 40;
+
+// [OCP] E4M3: log2 of the largest finite value 448, and log2 of its dynamic
+// range 448 / 2^-6 = 7 * 2^12 ([P1] eq. for the optimal k needs R_E4M3).
+constexpr float kLog2Max = 8.807354922057604f;     // log2(448)
+constexpr float kLog2Range = 14.807354922057604f;  // log2(28672)
+constexpr float kMaxK = 16.0f;                     // upper clamp of k
+
+// ------------------------------------------------- dequantization table
+// log2(|c| / 448) for every E4M3 magnitude byte, correctly rounded to FP32 at
+// compile time ([OCP] E4M3 values: (1 + f/8) 2^(e-7) for e > 0, f 2^-9 for
+// e = 0).  Dequantization reads it from LDS instead of taking log2 of the
+// decoded code, which is both cheaper and exact to half an FP32 ulp.
+
+constexpr double kLn2 = 0.69314718055994530941723212145818;
+
+// ln(x) for x >= 1: halve to [1, 2), then 2 atanh((x-1)/(x+1)) as a series.
+constexpr double cx_ln(double x) {
+  int e = 0;
+  while (x >= 2.0) {
+    x *= 0.5;
+    ++e;
+  }
+  const double z = (x - 1.0) / (x + 1.0);
+  const double z2 = z * z;
+  double term = z, sum = 0.0;
+  for (int n = 0; n < 60; ++n) {
+    sum += term / (2 * n + 1);
+    term *= z2;
+  }
+  return 2.0 * sum + e * kLn2;
+}
+
+constexpr double cx_log2(double x) { return cx_ln(x) / kLn2; }
+
+struct Log2Table {
+  float v[128];
+};
+
+constexpr Log2Table make_log2_table() {
+  Log2Table t{};
+  const double log2_max = cx_log2(7.0) + 6.0;  // log2 448
+  t.v[0] = -__builtin_huge_valf();                // code 0: 2^-inf = 0
+  for (int b = 1; b < 128; ++b) {
+    const int e = b >> 3, f = b & 7;
+    const double l = (e == 0) ? cx_log2((double)f) - 9.0
+                              : cx_log2(1.0 + f / 8.0) + (e - 7);
+    t.v[b] = (float)(l - log2_max);
+  }
+  t.v[127] = 0.0f;  // NaN code: outside the contract, read as the scale
+  return t;
+}
+
+__constant__ Log2Table kLog2Table = make_log2_table();
+
+// The same logarithms in double precision, for the exact dequantization of the
+// one element per group that decides k (see exact_min_key).
+struct Log2TableD {
+  double v[128];
+};
+
+constexpr Log2TableD make_log2_table_d() {
+  Log2TableD t{};
+  const double log2_max = cx_log2(7.0) + 6.0;
+  for (int b = 1; b < 127; ++b) {
+    const int e = b >> 3, f = b & 7;
+    const double l = (e == 0) ? cx_log2((double)f) - 9.0
+                              : cx_log2(1.0 + f / 8.0) + (e - 7);
+    t.v[b] = l - log2_max;
+  }
+  return t;
+}
+
+__constant__ Log2TableD kLog2TableD = make_log2_table_d();
+
+// Taylor coefficients of 2^f = e^(f ln2): (ln2)^i / i!, i = 0..13.
+struct Exp2Poly {
+  double c[14];
+};
+
+constexpr Exp2Poly make_exp2_poly() {
+  Exp2Poly p{};
+  double t = 1.0;
+  for (int i = 0; i < 14; ++i) {
+    p.c[i] = t;
+    t = t * kLn2 / (i + 1);
+  }
+  return p;
+}
+
+constexpr Exp2Poly kExp2Poly = make_exp2_poly();
+
+// 2^a in double: a = n + f with |f| <= 1/2; the degree-13 series leaves a
+// relative error below 1e-16 on that interval.
+__device__ __forceinline__ double exp2_f64(double a) {
+  const double n = __builtin_rint(a);
+  const double f = a - n;
+  double p = kExp2Poly.c[13];
+#pragma unroll
+  for (int i = 12; i >= 0; --i) p = __builtin_fma(p, f, kExp2Poly.c[i]);
+  return __builtin_ldexp(p, (int)n);
+}
+
+// sign(c) * s * (|c|/448)^(1/k) evaluated in double and rounded once to
+// FP32: the dequantized value exactly as a double-precision evaluation of the
+// definition rounds it ([P1] inverse of FP8量化 and of f).
+__device__ __forceinline__ float dequant_exact(uint32_t code, float scale, float k) {
+  const uint32_t mag = code & 0x7Fu;
+  if (!(scale > 0.0f) || !(k > 0.0f) || mag == 0u) return 0.0f;
+  const double a = kLog2TableD.v[mag] / (double)k;
+  const float x = (float)((double)scale * exp2_f64(a));
+  return (code & 0x80u) ? -x : x;
+}
+
+// b * x + omb * g with both products and the sum rounded to FP32, in that
+// order (no fused multiply-add), as [P1]'s AdamW moment update is written.
+__device__ __forceinline__ float moment_literal(float b, float x, float omb, float g) {
+#pragma clang fp contract(off)
+  return b * x + omb * g;
+}
+
+// Per-block copy in LDS, indexed by the whole code byte: {log2(|c|/448), sign}.
+__device__ __forceinline__ void load_log2_table(float2* tab) {
+  const int c = threadIdx.x;  // blockDim.x == 256
+  tab[c] = make_float2(kLog2Table.v[c & 0x7F], (c & 0x80) ? -1.0f : 1.0f);
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two E4M3 bytes of a word (bytes 0,1 or 2,3) as FP32 values, exact.
+template <bool kHigh>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHigh);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Group reductions over the G/16 lanes that hold one group (lanes are
+// consecutive and the group starts at a multiple of G/16).  Quad steps swap
+// lanes 1 and 2 apart; the third step mirrors each 8-lane half row, which
+// joins the two quads of a 128-element group.  Every lane ends with the
+// group's result.
+template <int kLanes>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) {
+  if constexpr (kLanes >= 2)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  if constexpr (kLanes >= 4)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  if constexpr (kLanes >= 8)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+template <int kLanes>
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t v) {
+  if constexpr (kLanes >= 2)
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  if constexpr (kLanes >= 4)
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  if constexpr (kLanes >= 8)
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// Running statistics of one lane for one moment: max |x| (FP32), and the
+// smallest nonzero |x| kept as the key 2*bits(|x|) - 2 modulo 2^32.  The key
+// sends +-0 to 0xFFFFFFFE, above every nonzero magnitude (non-negative floats
+// order like unsigned integers), so an unsigned min skips zeros ([P1] eq. for
+// R_X with the reading "min over nonzero").
+struct Stats {
+  float max_abs = 0.0f;
+  uint32_t min_key = 0xFFFFFFFFu;
+  __device__ __forceinline__ void add(float x) {
+    max_abs = __builtin_fmaxf(max_abs, fabsf(x));
+    min_key = min(min_key, (__float_as_uint(x) << 1) - 2u);
+  }
+  // Same, with the element's index j < 16 in the low 4 key bits: the minimum
+  // then names its element (ordering ignores magnitude differences below
+  // 2^-19 relative, which only matters for which element is re-evaluated).
+  __device__ __forceinline__ void add_indexed(float x, uint32_t j) {
+    max_abs = __builtin_fmaxf(max_abs, fabsf(x));
+    min_key = min(min_key, (((__float_as_uint(x) << 1) - 2u) & 0xFFFFFFF0u) | j);
+  }
+};
+
+constexpr uint32_t kEmptyKey = 0xFFFFFFF0u;  // keys at or above: no nonzero value
+
+// Dequantization constants of one group: x = sign(c) * s * 2^(L(c) / k) with
+// L(c) = log2(|c|/448) from the table.  This is s * (|c|/448)^(1/k), the
+// inverse of the quantizer followed by the inverse of f ([P1] FP8量化,
+// 动态范围扩展).
+struct DequantConst {
+  float s, rk, c0;
+};
+
+__device__ __forceinline__ DequantConst dequant_const(float scale, float k) {
+  DequantConst d;
+  const bool empty = !(scale > 0.0f) || !(k > 0.0f);
+  float rk = hw_rcp(k);
+  rk = fmaf(fmaf(-k, rk, 1.0f), rk, rk);  // one Newton step: 1/k to ~0.5 ulp
+  // The smallest nonzero code is 2^-9, so L reaches -(9 + log2 448) and the
+  // exponent L/k leaves FP32's normal range below k ~ 0.148; such groups
+  // shift the exponent up by 64 and the scale down by 2^64.
+  const bool shift = rk > 6.7f;
+  d.rk = empty ? 1.0f : rk;
+  d.c0 = (!empty && shift) ? 64.0f : 0.0f;
+  d.s = empty ? 0.0f : (shift ? scale * 0x1p-64f : scale);
+  return d;
+}
+
+// Magnitude of one element from its table entry (code 0: 2^-inf = 0).
+__device__ __forceinline__ float dequant_mag(float l, const DequantConst& d) {
+  return d.s * hw_exp2(fmaf(l, d.rk, d.c0));
+}
+
+// Quantization constants of one group: q = 2^(k * log2(|x| * P) + C), which
+// is 448 * (|x|/s)^k ([P1] f then FP8量化 with S = s^k / 448).
+struct QuantConst {
+  float p, k, c, scale;
+};
+
+__device__ __forceinline__ QuantConst quant_const(uint32_t max_bits, uint32_t min_key) {
+  QuantConst q;
+  const float s = __uint_as_float(max_bits);
+  if (!(s > 0.0f)) {  // empty group: scale 0, k 1, every code 0
+    q.p = 0.0f;
+    q.k = 1.0f;
+    q.c = kLog2Max;
+    q.scale = 0.0f;
+    return q;
+  }
+  const float mu = __uint_as_float((min_key >> 1) + 1u);
+  // log2(s / mu) = (exponent difference) + log2(mantissa ratio): exact
+  // integer part, and a logarithm of a number in (1/2, 2).
+  int es, em;
+  const float fs = frexpf(s, &es);
+  const float fm = frexpf(mu, &em);
+  const float lx = (float)(es - em) + hw_log2(fs * hw_rcp(fm));
+  // [P1] optimal k: (R_X)^k = R_E4M3; clamped above at 16 (also R_X = 1).
+  const float k = (lx > 0.0f) ? fminf(kMaxK, kLog2Range * hw_rcp(lx)) : kMaxK;
+  // |x| * P = 2^off * |x| / s; off keeps it inside FP32's normal range for
+  // very large or very small groups and for ranges above 2^100.
+  const int off = (s > 0x1p100f || lx > 100.0f) ? 64 : (s < 0x1p-100f ? -64 : 0);
+  q.p = hw_rcp(ldexpf(s, -off));
+  q.k = k;
+  q.c = kLog2Max - k * (float)off;
+  q.scale = s;
+  return q;
+}
+
+// |x| * P <= 2^off (1 + 2^-22), so the exponent stays within a few 1e-6 of
+// log2 448 at the group max: q <= 448 (1 + 4e-6), which the conversion rounds
+// to 448 (values up to 464 round to 448; no clamp needed).
+__device__ __forceinline__ float quant_mag(float x, const QuantConst& q) {
+  return hw_exp2(fmaf(q.k, hw_log2(fabsf(x) * q.p), q.c));
+}
+
+// Pack four signed magnitudes into four E4M3 bytes (round to nearest even).
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// ------------------------------------------------------------- step kernel
+
+struct TensorDesc {
+  float* w;
+  const uint16_t* g;
+  uint8_t* mc;
+  float* ms;
+  float* mk;
+  uint8_t* vc;
+  float* vs;
+  float* vk;
+  int64_t n;
+  int64_t tile_end;  // cumulative tile count up to and including this tensor
+};
+
+struct StepParams {
+  TensorDesc t[kMaxTensorsPerLaunch];
+  int64_t total_tiles;
+  float b1, b2;        // beta1, beta2
+  float omb1, omb2;    // 1 - beta1, 1 - beta2
+  // The update lr * (m_t/bc1) / (sqrt(v_t/bc2) + eps) is evaluated as
+  // m_t / (sqrt(v_t) * den_a + den_b) with den_a = 1/(sqrt(bc2) * lr/bc1) and
+  // den_b = eps / (lr/bc1); lr = 0 uses den_a = 0, den_b = +inf (no update).
+  float den_a;
+  float den_b;
+  float decay;         // 1 - lr * weight_decay
+};
+
+// Registers of one lane: 16 elements.
+struct LaneData {
+  float w[16];
+  uint32_t g[8];   // BF16 pairs
+  uint32_t mc[4];  // E4M3 codes, 4 per word
+  uint32_t vc[4];
+};
+
+constexpr int kExactRounds = 4;
+
+// Smallest nonzero |m_t| of the group as a key (2*bits - 2), evaluated
+// exactly for the candidate element; elements found to be exact zeros are
+// set to 0 in mt[] and skipped.  Returns a key >= kEmptyKey if the group has
+// no nonzero value.  `local` is this lane's indexed minimum key (see
+// Stats::add_indexed), `approx` the group's.  Control flow is wave-uniform.
+template <int kLanes>
+__device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, int64_t e0,
+                                                 const StepParams& p, float sm, float km,
+                                                 uint32_t local, uint32_t approx, float (&mt)[16]) {
+  uint32_t result = 0xFFFFFFFFu;
+  bool done = approx >= kEmptyKey;
+  uint32_t excluded = 0u;
+  for (int round = 0; round < kExactRounds; ++round) {
+    uint32_t key = 0xFFFFFFFFu;
+    if (!done && local == approx) {
+      const uint32_t j = approx & 0xFu;
+      const uint32_t code = T.mc[e0 + j];
+      const float g = __uint_as_float((uint32_t)T.g[e0 + j] << 16);
+      const float m = moment_literal(p.b1, dequant_exact(code, sm, km), p.omb1, g);
+      if (m == 0.0f) {
+        excluded |= 1u << j;
+        key = 0xFFFFFFFEu;  // "exact zero" marker, above every real key
+      } else {
+        key = (__float_as_uint(m) << 1) - 2u;
+      }
+    }
+    key = group_min_u32<kLanes>(key);
+    if (!done && key < kEmptyKey) {
+      result = key;
+      done = true;
+    }
+    if (__builtin_amdgcn_ballot_w64(!done) == 0) break;
+    // rescan this lane without the excluded elements
+    if (!done) {
+      uint32_t l2 = 0xFFFFFFFFu;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (!((excluded >> j) & 1u))
+          l2 = min(l2, (((__float_as_uint(mt[j]) << 1) - 2u) & 0xFFFFFFF0u) | (uint32_t)j);
+      local = l2;
+    }
+    approx = group_min_u32<kLanes>(local);
+    if (!done && approx >= kEmptyKey) done = true;  // only exact zeros remain
+  }
+  if (!done) result = approx & 0xFFFFFFF0u;  // rounds exhausted: FP32 minimum
+  if (__builtin_amdgcn_ballot_w64(excluded != 0u) != 0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if ((excluded >> j) & 1u) mt[j] = 0.0f;
+  }
+  return result;
+}
+
+template <bool kFull>
+__device__ __forceinline__ void load_lane(const TensorDesc& T, int64_t e0, LaneData& L) {
+  if constexpr (kFull) {
+    const float4* wp = reinterpret_cast<const float4*>(T.w + e0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = wp[q];
+      L.w[4 * q] = v.x;
+      L.w[4 * q + 1] = v.y;
+      L.w[4 * q + 2] = v.z;
+      L.w[4 * q + 3] = v.w;
+    }
+    const uint4* gp = reinterpret_cast<const uint4*>(T.g + e0);
+    const uint4 g0 = gp[0], g1 = gp[1];
+    L.g[0] = g0.x; L.g[1] = g0.y; L.g[2] = g0.z; L.g[3] = g0.w;
+    L.g[4] = g1.x; L.g[5] = g1.y; L.g[6] = g1.z; L.g[7] = g1.w;
+    const uint4 m = *reinterpret_cast<const uint4*>(T.mc + e0);
+    const uint4 v = *reinterpret_cast<const uint4*>(T.vc + e0);
+    L.mc[0] = m.x; L.mc[1] = m.y; L.mc[2] = m.z; L.mc[3] = m.w;
+    L.vc[0] = v.x; L.vc[1] = v.y; L.vc[2] = v.z; L.vc[3] = v.w;
+  } else {
+    // Tail tile: element-wise, zero padding past n.  Zeros leave max|x| and
+    // the nonzero minimum of a group unchanged.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) L.w[j] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) L.g[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { L.mc[j] = 0u; L.vc[j] = 0u; }
+    for (int j = 0; j < 16; ++j) {
+      const int64_t e = e0 + j;
+      if (e < T.n) {
+        L.w[j] = T.w[e];
+        L.g[j >> 1] |= (uint32_t)T.g[e] << (16 * (j & 1));
+        L.mc[j >> 2] |= (uint32_t)T.mc[e] << (8 * (j & 3));
+        L.vc[j >> 2] |= (uint32_t)T.vc[e] << (8 * (j & 3));
+      }
+    }
+  }
+}
+
+template <bool kFull>
+__device__ __forceinline__ void store_codes(uint8_t* base, int64_t e0, int64_t n,
+                                            const uint32_t (&c)[4]) {
+  if constexpr (kFull) {
+    *reinterpret_cast<uint4*>(base + e0) = make_uint4(c[0], c[1], c[2], c[3]);
+  } else {
+    for (int j = 0; j < 16; ++j)
+      if (e0 + j < n) base[e0 + j] = (uint8_t)(c[j >> 2] >> (8 * (j & 3)));
+  }
+}
+
+template <int G, bool kFull>
+__device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t e0, int lane,
+                                          const StepParams& p, const float2* tab) {
+  constexpr int kLanesPerGroup = G / kElemsPerLane;
+  const int64_t grp = e0 / G;
+  const int64_t ngroups = (T.n + G - 1) / G;
+  const bool grp_ok = kFull || grp < ngroups;
+
+  // a1: loads (all issued before any use)
+  LaneData L;
+  load_lane<kFull>(T, e0, L);
+  float sm = 0.0f, km = 0.0f, sv = 0.0f, kv = 0.0f;
+  if (grp_ok) {
+    sm = T.ms[grp];
+    km = T.mk[grp];
+    sv = T.vs[grp];
+    kv = T.vk[grp];
+  }
+
+  // a2: dequantize-expand both moments
+  const DequantConst dm = dequant_const(sm, km);
+  const DequantConst dv = dequant_const(sv, kv);
+  float mt[16], vt[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float2 em = tab[(L.mc[j >> 2] >> (8 * (j & 3))) & 0xFF];
+    const float lv = tab[(L.vc[j >> 2] >> (8 * (j & 3))) & 0xFF].x;
+    mt[j] = dequant_mag(em.x, dm) * em.y;
+    vt[j] = dequant_mag(lv, dv);  // second moment: codes carry no sign
+  }
+
+  // a3 + a4: moments, bias correction, weight update from unquantized m_t, v_t
+  Stats st_m, st_v;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float g = (j & 1) ? bf16_hi(L.g[j >> 1]) : bf16_lo(L.g[j >> 1]);
+    const float m = moment_literal(p.b1, mt[j], p.omb1, g);
+    const float v = fmaf(p.b2, vt[j], p.omb2 * (g * g));
+    const float den = fmaf(hw_sqrt(v), p.den_a, p.den_b);
+    L.w[j] = fmaf(L.w[j], p.decay, -(m * hw_rcp(den)));
+    mt[j] = m;
+    vt[j] = v;
+    st_m.add_indexed(m, (uint32_t)j);
+    st_v.add(v);
+  }
+  if constexpr (kFull) {
+    float4* wp = reinterpret_cast<float4*>(T.w + e0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      wp[q] = make_float4(L.w[4 * q], L.w[4 * q + 1], L.w[4 * q + 2], L.w[4 * q + 3]);
+  } else {
+    for (int j = 0; j < 16; ++j)
+      if (e0 + j < T.n) T.w[e0 + j] = L.w[j];
+  }
+
+  // a5: group statistics across the group's lanes
+  const uint32_t m_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_m.max_abs));
+  const uint32_t m_min_approx = group_min_u32<kLanesPerGroup>(st_m.min_key);
+  const uint32_t v_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_v.max_abs));
+  const uint32_t v_min = group_min_u32<kLanesPerGroup>(st_v.min_key);
+
+  // The first moment's smallest nonzero magnitude sets k, and it is usually
+  // the element where b1*m and (1-b1)*g cancel most, so an FP32 rounding
+  // difference in its dequantized m is magnified there.  The lane holding
+  // the group's FP32 minimum re-evaluates that one element exactly as the
+  // definition rounds it (dequantization in double rounded once, then the
+  // literal AdamW moment update).  If that value is exactly zero, the
+  // element is a zero, not the minimum: it is excluded and the next smallest
+  // element is tried (a few rounds, decided per wave).
+  const uint32_t m_min = exact_group_min<kLanesPerGroup>(T, e0, p, sm, km, st_m.min_key,
+                                                        m_min_approx, mt);
+
+  // a6: expansion exponent and scale per group (a group whose only nonzero
+  // first-moment values are exact zeros is empty)
+  const QuantConst qm = quant_const(m_min < kEmptyKey ? m_max : 0u, m_min);
+  const QuantConst qv = quant_const(v_max, v_min);
+
+  // a7: expand, scale, round, pack, store
+  uint32_t om[4], ov[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a[4], b[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = mt[4 * q + r];
+      a[r] = copysignf(quant_mag(x, qm), x);
+      b[r] = quant_mag(vt[4 * q + r], qv);
+    }
+    om[q] = pack4(a[0], a[1], a[2], a[3]);
+    ov[q] = pack4(b[0], b[1], b[2], b[3]);
+  }
+  store_codes<kFull>(T.mc, e0, T.n, om);
+  store_codes<kFull>(T.vc, e0, T.n, ov);
+  if ((lane % kLanesPerGroup) == 0 && grp_ok) {
+    T.ms[grp] = qm.scale;
+    T.mk[grp] = qm.k;
+    T.vs[grp] = qv.scale;
+    T.vk[grp] = qv.k;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kBlockThreads) void adamw_fp8_step_kernel(const StepParams p) {
+  __shared__ float2 tab[256];
+  load_log2_table(tab);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave =
+      (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  int ti = 0;
+  int64_t tile_begin = 0;
+  for (int64_t tile = wave; tile < p.total_tiles; tile += nwaves) {
+    while (tile >= p.t[ti].tile_end) {  // wave-uniform, monotone
+      tile_begin = p.t[ti].tile_end;
+      ++ti;
+    }
+    const TensorDesc& T = p.t[ti];
+    const int64_t local = tile - tile_begin;
+    const int64_t e0 = local * kTileElems + (int64_t)lane * kElemsPerLane;
+    if ((local + 1) * kTileElems <= T.n)
+      step_lane<G, true>(T, e0, lane, p, tab);
+    else
+      step_lane<G, false>(T, e0, lane, p, tab);
+  }
+}
+
+// ------------------------------------------- stand-alone quantize kernels
+
+struct CodecParams {
+  const float* x;  // expand_quantize input / dequantize output
+  float* xo;
+  uint8_t* codes;
+  const uint8_t* codes_in;
+  float* scale;
+  float* k;
+  const float* scale_in;
+  const float* k_in;
+  int64_t n;
+  int64_t tiles;
+};
+
+template <int G, bool kFull>
+__device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t e0, int lane) {
+  constexpr int kLanesPerGroup = G / kElemsPerLane;
+  const int64_t grp = e0 / G;
+  const bool grp_ok = kFull || grp < (p.n + G - 1) / G;
+  float x[16];
+  if constexpr (kFull) {
+    const float4* xp = reinterpret_cast<const float4*>(p.x + e0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = xp[q];
+      x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+  } else {
+    for (int j = 0; j < 16; ++j) x[j] = (e0 + j < p.n) ? p.x[e0 + j] : 0.0f;
+  }
+  Stats st;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.add(x[j]);
+  const QuantConst qc = quant_const(group_max_u32<kLanesPerGroup>(__float_as_uint(st.max_abs)),
+                                    group_min_u32<kLanesPerGroup>(st.min_key));
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float a[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = copysignf(quant_mag(x[4 * q + r], qc), x[4 * q + r]);
+    o[q] = pack4(a[0], a[1], a[2], a[3]);
+  }
+  store_codes<kFull>(p.codes, e0, p.n, o);
+  if ((lane % kLanesPerGroup) == 0 && grp_ok) {
+    p.scale[grp] = qc.scale;
+    p.k[grp] = qc.k;
+  }
+}
+
+template <int G, bool kFull>
+__device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t e0,
+                                                const float2* tab) {
+  const int64_t grp = e0 / G;
+  const bool grp_ok = kFull || grp < (p.n + G - 1) / G;
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  if constexpr (kFull) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p.codes_in + e0);
+    c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+  } else {
+    for (int j = 0; j < 16; ++j)
+      if (e0 + j < p.n) c[j >> 2] |= (uint32_t)p.codes_in[e0 + j] << (8 * (j & 3));
+  }
+  const DequantConst d = dequant_const(grp_ok ? p.scale_in[grp] : 0.0f,
+                                       grp_ok ? p.k_in[grp] : 0.0f);
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float2 e = tab[(c[j >> 2] >> (8 * (j & 3))) & 0xFF];
+    x[j] = dequant_mag(e.x, d) * e.y;
+  }
+  if constexpr (kFull) {
+    float4* xp = reinterpret_cast<float4*>(p.xo + e0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      xp[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+  } else {
+    for (int j = 0; j < 16; ++j)
+      if (e0 + j < p.n) p.xo[e0 + j] = x[j];
+  }
+}
+
+template <int G, bool kQuantize>
+__global__ __launch_bounds__(kBlockThreads) void codec_kernel(const CodecParams p) {
+  __shared__ float2 tab[256];
+  if constexpr (!kQuantize) load_log2_table(tab);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave =
+      (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
+  for (int64_t tile = wave; tile < p.tiles; tile += nwaves) {
+    const int64_t e0 = tile * kTileElems + (int64_t)lane * kElemsPerLane;
+    const bool full = (tile + 1) * kTileElems <= p.n;
+    if constexpr (kQuantize) {
+      if (full) quantize_lane<G, true>(p, e0, lane);
+      else quantize_lane<G, false>(p, e0, lane);
+    } else {
+      if (full) dequantize_lane<G, true>(p, e0, tab);
+      else dequantize_lane<G, false>(p, e0, tab);
+    }
+  }
+}
+
+// ------------------------------------------------ element-wise E4M3 cast
+
+__global__ __launch_bounds__(kBlockThreads) void e4m3_encode_kernel(const float* x, int64_t n,
+                                                                    uint8_t* codes) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float v = x[i];
+    const float c = copysignf(fminf(fabsf(v), 448.0f), v);  // saturate
+    codes[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false) & 0xFF);
+  }
+}
+
+__global__ __launch_bounds__(kBlockThreads) void e4m3_decode_kernel(const uint8_t* codes, int64_t n,
+                                                                    float* x) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    x[i] = __builtin_amdgcn_cvt_f32_fp8((int)codes[i], 0);
+}
+
+// ------------------------------------------------------------ host side
+
+thread_local char g_last_hip_error[256] = "";
+
+coat_status_t hip_fail(hipError_t e) {
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
+  return COAT_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_group_size(int32_t g) { return g == 16 || g == 32 || g == 64 || g == 128; }
+
+// Resident-block capacity of a kernel on the current device: the persistent
+// grid never exceeds it, so no block waits behind another's whole loop.
+struct LaunchShape {
+  int blocks_per_cu = 0;
+  int cus = 0;
+};
+
+std::mutex g_shape_mu;
+struct ShapeKey {
+  int device;
+  const void* fn;
+  LaunchShape shape;
+};
+std::vector<ShapeKey> g_shapes;
+
+hipError_t launch_shape(const void* fn, LaunchShape* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(g_shape_mu);
+    for (const ShapeKey& s : g_shapes)
+      if (s.device == dev && s.fn == fn) {
+        *out = s.shape;
+        return hipSuccess;
+      }
+  }
+  LaunchShape sh;
+  e = hipDeviceGetAttribute(&sh.cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&sh.blocks_per_cu, fn, kBlockThreads, 0);
+  if (e != hipSuccess) return e;
+  if (sh.blocks_per_cu < 1) sh.blocks_per_cu = 1;
+  std::lock_guard<std::mutex> lk(g_shape_mu);
+  g_shapes.push_back({dev, fn, sh});
+  *out = sh;
+  return hipSuccess;
+}
+
+hipError_t launch_persistent(const void* fn, int64_t tiles, void* arg, hipStream_t stream) {
+  LaunchShape sh;
+  hipError_t e = launch_shape(fn, &sh);
+  if (e != hipSuccess) return e;
+  const int64_t want = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int64_t cap = (int64_t)sh.cus * sh.blocks_per_cu;
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min(want, cap));
+  void* args[] = {arg};
+  return hipLaunchKernel(fn, dim3(blocks), dim3(kBlockThreads), args, 0, stream);
+}
+
+template <int G>
+const void* step_fn() {
+  return reinterpret_cast<const void*>(&adamw_fp8_step_kernel<G>);
+}
+
+const void* step_kernel_for(int32_t g) {
+  switch (g) {
+    case 16: return step_fn<16>();
+    case 32: return step_fn<32>();
+    case 64: return step_fn<64>();
+    default: return step_fn<128>();
+  }
+}
+
+template <bool kQuantize>
+const void* codec_kernel_for(int32_t g) {
+  switch (g) {
+    case 16: return reinterpret_cast<const void*>(&codec_kernel<16, kQuantize>);
+    case 32: return reinterpret_cast<const void*>(&codec_kernel<32, kQuantize>);
+    case 64: return reinterpret_cast<const void*>(&codec_kernel<64, kQuantize>);
+    default: return reinterpret_cast<const void*>(&codec_kernel<128, kQuantize>);
+  }
+}
+
+coat_status_t check_state(const coat_fp8_state_t& s) {
+  if (!s.codes || !s.scale || !s.k) return COAT_ERR_NULL_POINTER;
+  if (!aligned(s.codes, 16) || !aligned(s.scale, 4) || !aligned(s.k, 4)) return COAT_ERR_MISALIGNED;
+  return COAT_OK;
+}
+
+int64_t tiles_of(int64_t n) { return (n + kTileElems - 1) / kTileElems; }
+
+}  // namespace
+
+extern "C" {
+
+coat_status_t coat_adamw_fp8_step(const coat_adamw_tensor_t* tensors, int32_t num_tensors,
+                                  const coat_adamw_hparams_t* hp, hipStream_t stream) {
+  if (!hp) return COAT_ERR_NULL_POINTER;
+  if (num_tensors < 0) return COAT_ERR_INVALID_VALUE;
+  if (num_tensors > 0 && !tensors) return COAT_ERR_NULL_POINTER;
+  if (!valid_group_size(hp->group_size)) return COAT_ERR_GROUP_SIZE;
+  if (hp->step < 1 || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) ||
+      !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !isfinite(hp->lr) || !isfinite(hp->eps) ||
+      !isfinite(hp->weight_decay))
+    return COAT_ERR_INVALID_VALUE;
+  for (int32_t i = 0; i < num_tensors; ++i) {
+    const coat_adamw_tensor_t& t = tensors[i];
+    if (t.n < 0) return COAT_ERR_INVALID_VALUE;
+    if (t.n == 0) continue;
+    if (!t.w || !t.grad) return COAT_ERR_NULL_POINTER;
+    coat_status_t s = check_state(t.m);
+    if (s == COAT_OK) s = check_state(t.v);
+    if (s != COAT_OK) return s;
+    if (!aligned(t.w, 16) || !aligned(t.grad, 16)) return COAT_ERR_MISALIGNED;
+  }
+
+  // [P1] AdamW: bias corrections 1 - beta^t in double, then FP32 constants.
+  StepParams p;
+  memset(&p, 0, sizeof(p));
+  const double bc1 = 1.0 - pow((double)hp->beta1, (double)hp->step);
+  const double bc2 = 1.0 - pow((double)hp->beta2, (double)hp->step);
+  p.b1 = hp->beta1;
+  p.b2 = hp->beta2;
+  p.omb1 = 1.0f - hp->beta1;
+  p.omb2 = 1.0f - hp->beta2;
+  const double lr_bc1 = (double)hp->lr / (double)(float)bc1;
+  if (lr_bc1 != 0.0) {
+    p.den_a = (float)(1.0 / (sqrt((double)(float)bc2) * lr_bc1));
+    p.den_b = (float)((double)hp->eps / lr_bc1);
+  } else {
+    p.den_a = 0.0f;
+    p.den_b = INFINITY;
+  }
+  p.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+
+  const void* fn = step_kernel_for(hp->group_size);
+  int used = 0;
+  int64_t tiles = 0;
+  for (int32_t i = 0; i < num_tensors; ++i) {
+    const coat_adamw_tensor_t& t = tensors[i];
+    if (t.n == 0) continue;
+    TensorDesc& d = p.t[used++];
+    d.w = t.w;
+    d.g = t.grad;
+    d.mc = t.m.codes;
+    d.ms = t.m.scale;
+    d.mk = t.m.k;
+    d.vc = t.v.codes;
+    d.vs = t.v.scale;
+    d.vk = t.v.k;
+    d.n = t.n;
+    tiles += tiles_of(t.n);
+    d.tile_end = tiles;
+    if (used == kMaxTensorsPerLaunch) {
+      p.total_tiles = tiles;
+      const hipError_t e = launch_persistent(fn, tiles, &p, stream);
+      if (e != hipSuccess) return hip_fail(e);
+      used = 0;
+      tiles = 0;
+    }
+  }
+  if (used > 0) {
+    p.total_tiles = tiles;
+    // descriptors past `used` are never reached: tile < total_tiles
+    const hipError_t e = launch_persistent(fn, tiles, &p, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return COAT_OK;
+}
+
+coat_status_t coat_fp8_expand_quantize(const float* x, int64_t n, int32_t group_size,
+                                       coat_fp8_state_t out, hipStream_t stream) {
+  if (n < 0) return COAT_ERR_INVALID_VALUE;
+  if (!valid_group_size(group_size)) return COAT_ERR_GROUP_SIZE;
+  if (n == 0) return COAT_OK;
+  if (!x) return COAT_ERR_NULL_POINTER;
+  const coat_status_t s = check_state(out);
+  if (s != COAT_OK) return s;
+  if (!aligned(x, 16)) return COAT_ERR_MISALIGNED;
+  CodecParams p;
+  memset(&p, 0, sizeof(p));
+  p.x = x;
+  p.codes = out.codes;
+  p.scale = out.scale;
+  p.k = out.k;
+  p.n = n;
+  p.tiles = tiles_of(n);
+  const hipError_t e = launch_persistent(codec_kernel_for<true>(group_size), p.tiles, &p, stream);
+  return e == hipSuccess ? COAT_OK : hip_fail(e);
+}
+
+coat_status_t coat_fp8_dequantize_expand(const uint8_t* codes, const float* scale,
+                                         const float* k, int64_t n, int32_t group_size,
+                                         float* x, hipStream_t stream) {
+  if (n < 0) return COAT_ERR_INVALID_VALUE;
+  if (!valid_group_size(group_size)) return COAT_ERR_GROUP_SIZE;
+  if (n == 0) return COAT_OK;
+  if (!codes || !scale || !k || !x) return COAT_ERR_NULL_POINTER;
+  if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(scale, 4) || !aligned(k, 4))
+    return COAT_ERR_MISALIGNED;
+  CodecParams p;
+  memset(&p, 0, sizeof(p));
+  p.codes_in = codes;
+  p.scale_in = scale;
+  p.k_in = k;
+  p.xo = x;
+  p.n = n;
+  p.tiles = tiles_of(n);
+  const hipError_t e = launch_persistent(codec_kernel_for<false>(group_size), p.tiles, &p, stream);
+  return e == hipSuccess ? COAT_OK : hip_fail(e);
+}
+
+coat_status_t coat_e4m3_encode(const float* x, int64_t n, uint8_t* codes, hipStream_t stream) {
+  if (n < 0) return COAT_ERR_INVALID_VALUE;
+  if (n == 0) return COAT_OK;
+  if (!x || !codes) return COAT_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return COAT_ERR_MISALIGNED;
+  const int64_t blocks = std::min<int64_t>((n + kBlockThreads - 1) / kBlockThreads, 1 << 16);
+  hipLaunchKernelGGL(e4m3_encode_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, stream, x,
+                     n, codes);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? COAT_OK : hip_fail(e);
+}
+
+coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x, hipStream_t stream) {
+  if (n < 0) return COAT_ERR_INVALID_VALUE;
+  if (n == 0) return COAT_OK;
+  if (!x || !codes) return COAT_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(codes, 16)) return COAT_ERR_MISALIGNED;
+  const int64_t blocks = std::min<int64_t>((n + kBlockThreads - 1) / kBlockThreads, 1 << 16);
+  hipLaunchKernelGGL(e4m3_decode_kernel, dim3((unsigned)blocks), dim3(kBlockThreads), 0, stream,
+                     codes, n, x);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? COAT_OK : hip_fail(e);
+}
+
+const char* coat_status_string(coat_status_t status) {
+  switch (status) {
+    case COAT_OK: return "COAT_OK";
+    case COAT_ERR_NULL_POINTER: return "COAT_ERR_NULL_POINTER: a required pointer is NULL";
+    case COAT_ERR_INVALID_VALUE: return "COAT_ERR_INVALID_VALUE: bad size, step or hyperparameter";
+    case COAT_ERR_GROUP_SIZE: return "COAT_ERR_GROUP_SIZE: group_size must be 16, 32, 64 or 128";
+    case COAT_ERR_MISALIGNED: return "COAT_ERR_MISALIGNED: arrays must be 16-byte (scale/k 4-byte) aligned";
+    case COAT_ERR_HIP: return "COAT_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown coat_status_t";
+}
+
+const char* coat_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t coat_abi_version(void) { return COAT_FP8_ABI_VERSION; }
+
+}  // extern "C"

@@ -178,3 +178,20 @@ def bf16_bits(t: torch.Tensor) -> torch.Tensor:
     """Raw uint16 view of a BF16 tensor (int16 storage reinterpreted)."""
     assert t.dtype == torch.bfloat16
     return t.view(torch.int16)
+
+
+# ------------------------------------------------ filling a flat shard
+# A "shard" is any object with flat device buffers `w` (float32) and `grad`
+# (bfloat16) and per-tensor `element_range(i)` slices (see shard.py).
+
+def fill_weights(shard, seed: int = 0):
+    for i in range(len(shard.numels)):
+        e = shard.element_range(i)
+        shard.w[e].copy_(weights(shard.numels[i], i, shard.w.device, seed=seed))
+
+
+def fill_gradients(shard, step: int, stds: Sequence[float], kind: str = "gaussian"):
+    for i in range(len(shard.numels)):
+        e = shard.element_range(i)
+        shard.grad[e].copy_(gradient(shard.numels[i], stds[i], step, i, shard.grad.device,
+                                     kind=kind, group_size=shard.group_size))

@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused FP8 AdamW step (COAT, dynamic range expansion) on one
+MI355X.
+
+A step is one call of the whole hot path over the whole workload: dequantize
+m and v, AdamW on FP32 master weights from BF16 gradients, per-group
+max/min-nonzero, k and scale, re-quantize to E4M3 -- for every tensor.
+
+Workload (default): the Llama-2-7B-shaped parameter list on one GPU
+(291 tensors, 6,738,415,616 parameters, G = 128), all buffers resident in HBM,
+synthetic seeded data (w ~ N(0, 0.02); per-tensor gradient std log-uniform in
+[1e-5, 1e-2]; BF16 gradients).  Warm-up steps draw a fresh gradient each step
+(state history), the timed steps reuse the last gradient (its values do not
+change the work or the traffic).
+
+Prints ONE JSON line: Gparam/s over the timed steps, plus the step kernel's
+roofline position (algorithmic bytes per launch / average launch duration,
+HIP events on the launch stream) and the CPU oracle timed on a bounded sample
+on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_adamw_fp8_step_llama2_7b.txt")
+KERNEL_SRC = os.path.join(ROOT, "adamw_coat_fp8_amd", "csrc", "coat_fp8.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--group-size", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=128 * 1024 * 1024,
+                    help="parameters in the oracle's timing sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of known size (PMC calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(n: int, G: int) -> int:
+    """Per tensor: read w 4 + g 2 + m 1 + v 1, write w 4 + m 1 + v 1 bytes per
+    element; per group read and write scale and k of both moments (32 B)."""
+    return 14 * n + 32 * ((n + G - 1) // G)
+
+
+def kernel_source_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(nbytes_per_launch):
+    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(specs, G, hp, sample_params):
+    """The oracle, as it stands, timed on a bounded sample of the workload:
+    the first elements of each tensor (up to 2M per tensor) until the sample is
+    full; warm state from one untimed oracle step; one timed step.  Threads
+    split the sample by whole tensors-slices (the oracle is single-threaded
+    C; ctypes releases the GIL)."""
+    import numpy as np
+    import oracle
+    from adamw_coat_fp8_amd import inputs
+
+    stds = inputs.grad_stds(len(specs))
+    pieces, left = [], sample_params
+    for i, s in enumerate(specs):
+        if left <= 0:
+            break
+        n = min(s.numel, 2 * 1024 * 1024, left)
+        n -= n % G if n >= G else 0
+        pieces.append((i, n))
+        left -= n
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    work = []
+    for i, n in pieces:
+        w = inputs.weights(n, i, "cpu").numpy().copy()
+        g1 = inputs.bf16_bits(inputs.gradient(n, stds[i], 1, i, "cpu")).numpy().view(np.uint16).copy()
+        g2 = inputs.bf16_bits(inputs.gradient(n, stds[i], 2, i, "cpu")).numpy().view(np.uint16).copy()
+        work.append([w, g1, g2, oracle.QuantizedState.zeros(n, G), oracle.QuantizedState.zeros(n, G)])
+
+    def run(item, step):
+        w, g1, g2, m, v = item
+        oracle.adamw_fp8_step(w, g1 if step == 1 else g2, m, v, G, **hp, step=step)
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda it: run(it, 1), work))
+        t0 = time.perf_counter()
+        list(ex.map(lambda it: run(it, 2), work))
+        dt = time.perf_counter() - t0
+    n_total = sum(n for _, n in pieces)
+    return {"value": n_total / dt / 1e9, "unit": "Gparam/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_total} params: first <=2M elements of the first {len(pieces)} "
+                      f"tensors, one warm step (after one untimed step), {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the step is shard-local and would run unchanged on each GPU's shard.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from adamw_coat_fp8_amd import coat, inputs
+    from adamw_coat_fp8_amd.shard import FP8AdamWShard
+
+    G = args.group_size
+    hp = dict(inputs.DEFAULT_HPARAMS)
+    specs = inputs.workload_specs(args.workload)
+    numels = [s.numel for s in specs]
+    n_params = sum(numels)
+    print(f"[bench] workload {args.workload}: {len(specs)} tensors, {n_params} params, "
+          f"G={G}", file=sys.stderr, flush=True)
+    torch.cuda.init()
+    shard = FP8AdamWShard(numels, group_size=G, device="cuda")
+    stds = inputs.grad_stds(len(specs))
+    inputs.fill_weights(shard)
+    call_lists = shard.calls
+    call_bytes = [sum(algorithmic_bytes(numels[i], G) for i in c) for c in shard.call_indices]
+    stream = torch.cuda.current_stream()
+
+    def step(t, events=None):
+        shard.step(t, **hp, stream=stream, events=events)
+
+    t = 0
+    for w in range(args.warmup):
+        t += 1
+        inputs.fill_gradients(shard, t, stds)
+        step(t)
+        torch.cuda.synchronize()
+        print(f"[bench] warm-up step {t} done", file=sys.stderr, flush=True)
+    if args.warmup == 0:
+        inputs.fill_gradients(shard, 1, stds)
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in call_lists] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        t += 1
+        step(t, events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = [[events[k][j][0].elapsed_time(events[k][j][1]) for j in range(len(call_lists))]
+                 for k in range(args.steps)]
+    avg_launch_ms = sum(sum(r) for r in launch_ms) / (args.steps * len(call_lists))
+    bytes_per_launch = sum(call_bytes) / len(call_lists)
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    print(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step, "
+          f"{len(call_lists)} launches/step, avg launch {avg_launch_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy probe: 3 x 4 GiB device copies done", file=sys.stderr, flush=True)
+        del src, dst
+
+    traffic = traffic_from_profile(bytes_per_launch)
+    value = n_params / (ms_per_step * 1e-3) / 1e9
+    total_bytes = sum(call_bytes)
+    rec = {
+        "metric": "Gparam/s per fused FP8-AdamW step + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(value, 3),
+        "unit": "Gparam/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {len(specs)} tensors, {n_params} params, FP32 "
+                        f"master weights, BF16 grads, E4M3 m/v with per-group FP32 scale and k",
+            "group_size": G,
+            "hparams": hp,
+            "step_hbm_GBps": round(total_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+            "step_frac_of_peak": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": total_bytes,
+            "launches_per_step": len(call_lists),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": f"adamw_fp8_step_kernel<{G}>",
+            "bytes_per_launch": int(bytes_per_launch),
+            "avg_launch_ms": round(avg_launch_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(specs, G, hp, args.cpu_sample)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

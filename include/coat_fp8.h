@@ -1,0 +1,160 @@
+/*
+ * coat_fp8.h -- C ABI of the MI355X (gfx950) FP8 AdamW optimizer step with
+ * Dynamic Range Expansion (COAT, arXiv:2410.19313).
+ *
+ * Sources, cited by page and section:
+ *   [P1] "COAT: Compressing Optimizer States and Activation for Memory-Efficient
+ *        FP8 Training", paper review at xllm-io.github.io.  Section 三
+ *        (技术架构) / 核心公式: quantizer equation "FP8量化", AdamW equation
+ *        "AdamW优化器更新规则", expansion equations under "动态范围扩展"
+ *        (f(x) = sign(x)|x|^k, R_f(X) = (R_X)^k, optimal k = log_{R_X} R_E4M3).
+ *        Section 四 table: the optimizer state update is one fused kernel, and
+ *        under FSDP each GPU handles its own shard with no cross-GPU range sync.
+ *   [OCP] OCP 8-bit Floating Point Specification (OFP8): E4M3, bias 7,
+ *        largest finite 448, smallest normal 2^-6, no infinities.
+ *
+ * State layout (one "moment" = m or v of one tensor of n elements, group size G):
+ *   codes[n]            E4M3 codes, element i in byte i.  Sign in bit 7.
+ *   scale[ceil(n/G)]    FP32: the group's max |x| before expansion.  0 marks an
+ *                       all-zero group (k is then ignored).
+ *   k[ceil(n/G)]        FP32: the group's expansion exponent, 0 < k <= 16.
+ * Group j covers elements [j*G, min(n, (j+1)*G)).  Groups never cross tensors.
+ * A value is stored as code = RNE_E4M3(448 * (|x|/scale)^k) with the sign of x
+ * and read back as x = sign(code) * scale * (|code|/448)^(1/k).  Fresh state is
+ * all-zero bytes (scale 0 everywhere).
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is DEVICE memory owned by the caller.  The library
+ *     allocates nothing, keeps no per-call state, never synchronizes and never
+ *     copies host<->device.  Host structs passed by pointer are read during the
+ *     call only.
+ *   - Work is enqueued on `stream` (0 = the null stream); results are valid
+ *     once the caller synchronizes with that stream.
+ *   - Arrays must not alias each other.  Codes, FP32 and BF16 element arrays
+ *     must be 16-byte aligned; scale and k arrays 4-byte aligned.
+ *   - Validation runs before anything is enqueued: any status other than
+ *     COAT_ERR_HIP means nothing was launched and no buffer was touched.
+ *     COAT_ERR_HIP means a launch failed (earlier launches of the same call may
+ *     have run; the state is then undefined).
+ *   - n == 0 is a successful no-op (pointers may then be NULL).
+ *   - NaN or Inf in inputs is outside the contract.  Exactness (parity with the
+ *     CPU reference to the documented tolerance) holds for groups whose
+ *     dynamic range max|x| / min-nonzero|x| is at most 2^157.
+ */
+#ifndef COAT_FP8_H
+#define COAT_FP8_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COAT_FP8_ABI_VERSION 1
+
+typedef enum coat_status {
+  COAT_OK = 0,
+  COAT_ERR_NULL_POINTER = 1,  /* a required pointer is NULL                 */
+  COAT_ERR_INVALID_VALUE = 2, /* negative size, bad hyperparameter or step  */
+  COAT_ERR_GROUP_SIZE = 3,    /* group_size not in {16, 32, 64, 128}         */
+  COAT_ERR_MISALIGNED = 4,    /* an array violates the alignment rule above */
+  COAT_ERR_HIP = 5            /* a HIP launch failed                        */
+} coat_status_t;
+
+/* One quantized moment (see "State layout"). */
+typedef struct coat_fp8_state {
+  uint8_t* codes;
+  float* scale;
+  float* k;
+} coat_fp8_state_t;
+
+/* One parameter tensor of an optimizer shard. */
+typedef struct coat_adamw_tensor {
+  float* w;              /* n FP32 master weights, updated in place      */
+  const uint16_t* grad;  /* n BF16 gradient bit patterns, read only      */
+  coat_fp8_state_t m;    /* first moment, updated in place               */
+  coat_fp8_state_t v;    /* second moment, updated in place              */
+  int64_t n;             /* number of elements, >= 0                     */
+} coat_adamw_tensor_t;
+
+typedef struct coat_adamw_hparams {
+  float lr;           /* eta, finite                                       */
+  float beta1;        /* in [0, 1)                                         */
+  float beta2;        /* in [0, 1)                                         */
+  float eps;          /* added to sqrt(v_hat), finite                      */
+  float weight_decay; /* lambda, decoupled: w -= lr * lambda * w, finite   */
+  int64_t step;       /* t of this update, >= 1; the caller increments it  */
+  int32_t group_size; /* G in {16, 32, 64, 128}                            */
+} coat_adamw_hparams_t;
+
+/*
+ * One fused AdamW step over a list of tensors ([P1] section 四: fused
+ * optimizer kernel; [P1] 核心公式 AdamW, FP8量化 and 动态范围扩展).
+ * Per group: dequantize m and v (invert the quantizer, then f), apply
+ *   m_t = b1 m + (1-b1) g,  v_t = b2 v + (1-b2) g^2,
+ *   w  <- w - lr ( (m_t/(1-b1^t)) / (sqrt(v_t/(1-b2^t)) + eps) + wd w ),
+ * using the unquantized m_t and v_t, then store m_t and v_t again with a
+ * fresh scale = max|x| and k = min(16, log2(448/2^-6) / log2(max|x|/min|x|))
+ * (min over nonzero |x|; k = 16 when all nonzero magnitudes are equal).
+ * The step is shard-local: it reads and writes only the given tensors.
+ * Errors: COAT_ERR_NULL_POINTER (tensors/hp NULL, or a pointer of a tensor
+ * with n > 0), COAT_ERR_INVALID_VALUE (num_tensors < 0, n < 0, step < 1,
+ * beta outside [0,1), non-finite lr/eps/weight_decay), COAT_ERR_GROUP_SIZE,
+ * COAT_ERR_MISALIGNED, COAT_ERR_HIP.
+ */
+coat_status_t coat_adamw_fp8_step(const coat_adamw_tensor_t* tensors,
+                                  int32_t num_tensors,
+                                  const coat_adamw_hparams_t* hp,
+                                  hipStream_t stream);
+
+/*
+ * Expand and quantize an FP32 vector into a fresh state ([P1] 核心公式:
+ * FP8量化 applied per group to f(X) with the group's optimal k).  Used to
+ * convert FP32 optimizer states (e.g. a checkpoint) into FP8 state.
+ * x: n FP32 values (read only).  out: codes[n], scale/k[ceil(n/G)] (written).
+ * Errors: NULL_POINTER, INVALID_VALUE (n < 0), GROUP_SIZE, MISALIGNED, HIP.
+ */
+coat_status_t coat_fp8_expand_quantize(const float* x, int64_t n,
+                                       int32_t group_size, coat_fp8_state_t out,
+                                       hipStream_t stream);
+
+/*
+ * Dequantize and un-expand a state into FP32 ([P1] 核心公式: inverse of the
+ * quantizer, then of f): x = sign(c) * scale * (|c|/448)^(1/k); a group with
+ * scale 0 reads as zeros.  codes/scale/k read only; x[n] written.
+ * Errors: NULL_POINTER, INVALID_VALUE (n < 0), GROUP_SIZE, MISALIGNED, HIP.
+ */
+coat_status_t coat_fp8_dequantize_expand(const uint8_t* codes,
+                                         const float* scale, const float* k,
+                                         int64_t n, int32_t group_size,
+                                         float* x, hipStream_t stream);
+
+/*
+ * Plain OCP E4M3 conversion, element-wise ([OCP]; the rounding step the
+ * quantizer ends in): codes[i] = round-to-nearest-even(x[i]), saturating at
+ * +-448, sign kept (a negative value that rounds to zero gives 0x80).
+ * Errors: NULL_POINTER, INVALID_VALUE (n < 0), MISALIGNED, HIP.
+ */
+coat_status_t coat_e4m3_encode(const float* x, int64_t n, uint8_t* codes,
+                               hipStream_t stream);
+
+/* Inverse of the above: x[i] = value of codes[i] (NaN for 0x7F / 0xFF). */
+coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x,
+                               hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* coat_status_string(coat_status_t status);
+
+/* HIP error string of the last COAT_ERR_HIP returned on the calling thread
+ * (empty string if none). */
+const char* coat_last_hip_error(void);
+
+/* COAT_FP8_ABI_VERSION of the loaded library. */
+int32_t coat_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COAT_FP8_H */

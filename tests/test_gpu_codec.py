@@ -1,0 +1,123 @@
+"""GPU parity of the codec entry points against the oracle: the element-wise
+E4M3 cast (bit-exact), stand-alone dequantize-expand (relative error bound)
+and expand-quantize (scale exact, k within 1e-5, codes identical except near
+ties)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, lib, require_gpu, to_dev_state
+from parity import REL_TOL, _check_state, dequant_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module():
+    require_gpu()
+
+
+def test_decode_all_codes_bit_exact():
+    coat = lib()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).to(DEV)
+    x = torch.empty(256, dtype=torch.float32, device=DEV)
+    coat.e4m3_decode(codes, x)
+    got = x.cpu().numpy().astype(np.float64)
+    ref = oracle.e4m3_decode_array(np.arange(256))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _encode_gpu(x_np):
+    coat = lib()
+    x = torch.from_numpy(np.ascontiguousarray(x_np, np.float32)).to(DEV)
+    c = torch.empty(x.numel(), dtype=torch.uint8, device=DEV)
+    coat.e4m3_encode(x, c)
+    return c.cpu().numpy()
+
+
+def test_encode_dense_sweep_bit_exact():
+    # every 7th FP32 bit pattern in [0, 448] (~163M values) and their negatives
+    # would be slow on the host; take every 997th plus all near-tie values
+    bits = np.arange(0, 0x43E00001, 997, dtype=np.uint32)
+    x = bits.view(np.float32)
+    table = np.unique(np.abs(oracle.e4m3_decode_array(np.arange(0x7F))))
+    mids = (table[:-1] + table[1:]) / 2
+    near = []
+    for m in mids.astype(np.float32):
+        v = m
+        for _ in range(4):
+            v = np.nextafter(v, np.float32(0))
+        for _ in range(9):
+            near.append(v)
+            v = np.nextafter(v, np.float32(1e9))
+    x = np.concatenate([x, np.array(near, np.float32), table.astype(np.float32),
+                        np.array([448.0, 460.0, 463.99, 1e6, 3e38], np.float32)])
+    for sgn in (1.0, -1.0):
+        xs = (sgn * x).astype(np.float32)
+        got = _encode_gpu(xs)
+        ref = oracle.e4m3_encode_array(xs.astype(np.float64))
+        # signed zero: the oracle gives 0x00 for -0.0
+        zero = xs == 0
+        assert np.array_equal(got[~zero], ref[~zero])
+        assert np.all((got[zero] & 0x7F) == 0)
+
+
+def _random_groups(rng, n, G, spreads):
+    x = np.empty(n, np.float32)
+    for g0 in range(0, n, G):
+        sp = spreads[(g0 // G) % len(spreads)]
+        L = min(G, n - g0)
+        mag = np.exp2(rng.uniform(-sp / 2, sp / 2, L) + rng.uniform(-30, 5))
+        x[g0:g0 + L] = mag * np.where(rng.random(L) < 0.5, -1, 1)
+    x[rng.random(n) < 0.05] = 0.0
+    return x
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+@pytest.mark.parametrize("n", [1, 1000, 4096, 70000 + 3])
+def test_dequantize_matches_oracle(G, n):
+    coat = lib()
+    rng = np.random.default_rng(G * 7 + n)
+    x = _random_groups(rng, n, G, [0.5, 4, 10, 20, 40, 100])
+    st = oracle.expand_quantize(x, G)
+    ref = oracle.dequantize_expand(st, G).astype(np.float64)
+    out = torch.empty(n, dtype=torch.float32, device=DEV)
+    coat.dequantize_expand(to_dev_state(st), out, G)
+    got = out.cpu().numpy().astype(np.float64)
+    zero = ref == 0
+    assert np.array_equal(got[zero], ref[zero])
+    rel = np.abs(got[~zero] - ref[~zero]) / np.abs(ref[~zero])
+    bound = dequant_bound(st, G)[~zero]
+    print(f"[dequant] G={G} n={n}: max rel err {rel.max(initial=0):.2e}, "
+          f"max rel err / bound {np.max(rel / bound, initial=0):.2f}", flush=True)
+    assert np.all(rel <= bound)
+    assert rel.max(initial=0) <= REL_TOL
+    assert np.array_equal(np.signbit(got[~zero]), np.signbit(ref[~zero]))
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+@pytest.mark.parametrize("n", [1, 17, 1000, 65536, 70000 + 3])
+def test_expand_quantize_matches_oracle(G, n):
+    coat = lib()
+    rng = np.random.default_rng(G * 13 + n)
+    x = _random_groups(rng, n, G, [0.0, 0.5, 4, 10, 14.8, 20, 40, 100])
+    if n > 100:
+        x[:G] = 0.0                       # an all-zero group
+        x[G:2 * G] = 0.0
+        x[G + 3] = -2.5e-9                 # a single-nonzero group
+    ref = oracle.expand_quantize(x, G)
+    out = coat.QuantState.zeros(n, G, DEV)
+    coat.expand_quantize(torch.from_numpy(x).to(DEV), out, G)
+    torch.cuda.synchronize()
+    gs, gk = out.scale.cpu().numpy(), out.k.cpu().numpy()
+    assert np.array_equal(gs, ref.scale)          # max|x| is exact
+    rep = {}
+    # inputs are exact on both sides: zero-width box, only near-tie slack
+    _check_state("x", out.codes.cpu().numpy(), gs, gk, ref, x, np.zeros(n), np.zeros(n), G,
+                 rep, signed=True)
+    nz = ref.scale > 0
+    assert np.all(np.abs(gk[nz] - ref.k[nz]) <= 1e-5 * ref.k[nz])
+    assert np.all(gk[~nz] == 1.0)

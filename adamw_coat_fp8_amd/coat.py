@@ -58,12 +58,12 @@ class AdamWHParams(ctypes.Structure):
                 ("group_size", ctypes.c_int32)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -c \"import "
+            f"{path} is missing: build it with `python -c \"import "
             f"__graft_entry__; __graft_entry__.build()\"` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.coat_adamw_fp8_step.restype = ctypes.c_int
     lib.coat_adamw_fp8_step.argtypes = [vp, i32, ctypes.POINTER(AdamWHParams), vp]
@@ -82,7 +82,7 @@ def _load():
     lib.coat_abi_version.restype = ctypes.c_int32
     lib.coat_abi_version.argtypes = []
     if lib.coat_abi_version() != ABI_VERSION:
-        raise ImportError(f"{LIB_PATH}: ABI version {lib.coat_abi_version()}, "
+        raise ImportError(f"{path}: ABI version {lib.coat_abi_version()}, "
                           f"binding expects {ABI_VERSION}")
     return lib
 

@@ -10,13 +10,14 @@
 //
 // Execution model.  The step is an element-wise update plus a per-group
 // reduction, bound by HBM bandwidth (about 14 bytes per parameter), so it uses
-// no matrix cores and no LDS.  One 64-lane wavefront owns a "tile" of 1024
-// consecutive elements of one tensor; each lane owns 16 consecutive elements,
-// so a group of G elements lives in G/16 neighbouring lanes and its max /
-// min reductions are 0..3 DPP steps inside registers.  Per lane, every stream
-// moves in 16-byte accesses: w 4 x 16 B, g 2 x 16 B, codes 1 x 16 B each.
-// Waves walk the tiles of all tensors of one launch with a grid stride;
-// tensor descriptors travel in the kernel arguments.
+// no matrix cores.  One 64-lane wavefront owns a "tile" of 1024 consecutive
+// elements of one tensor; each lane owns 16 elements of one group, so a group
+// of G elements lives in G/16 neighbouring lanes and its max / min reductions
+// are 0..3 DPP steps inside registers (see LaneMap for the interleave that
+// keeps every memory instruction on whole cache lines).  LDS holds only a
+// 2 KB table for dequantization.  Waves walk the tiles of all tensors of one
+// launch with a grid stride; tensor descriptors travel in the kernel
+// arguments.
 
 #include <hip/hip_runtime.h>
 
@@ -112,42 +113,39 @@ constexpr Log2TableD make_log2_table_d() {
 
 __constant__ Log2TableD kLog2TableD = make_log2_table_d();
 
-// Taylor coefficients of 2^f = e^(f ln2): (ln2)^i / i!, i = 0..13.
-struct Exp2Poly {
-  double c[14];
-};
+// Taylor coefficients of 2^f = e^(f ln2): (ln2)^i / i!, i = 0..13.  They
+// reach the kernel in its arguments (scalar registers): as compile-time
+// constants they would be held in vector registers for the whole kernel.
+constexpr int kExp2Terms = 14;
 
-constexpr Exp2Poly make_exp2_poly() {
-  Exp2Poly p{};
+void exp2_coefficients(double* c) {
   double t = 1.0;
-  for (int i = 0; i < 14; ++i) {
-    p.c[i] = t;
+  for (int i = 0; i < kExp2Terms; ++i) {
+    c[i] = t;
     t = t * kLn2 / (i + 1);
   }
-  return p;
 }
-
-constexpr Exp2Poly kExp2Poly = make_exp2_poly();
 
 // 2^a in double: a = n + f with |f| <= 1/2; the degree-13 series leaves a
 // relative error below 1e-16 on that interval.
-__device__ __forceinline__ double exp2_f64(double a) {
+__device__ __forceinline__ double exp2_f64(double a, const double* coef) {
   const double n = __builtin_rint(a);
   const double f = a - n;
-  double p = kExp2Poly.c[13];
+  double p = coef[kExp2Terms - 1];
 #pragma unroll
-  for (int i = 12; i >= 0; --i) p = __builtin_fma(p, f, kExp2Poly.c[i]);
+  for (int i = kExp2Terms - 2; i >= 0; --i) p = __builtin_fma(p, f, coef[i]);
   return __builtin_ldexp(p, (int)n);
 }
 
 // sign(c) * s * (|c|/448)^(1/k) evaluated in double and rounded once to
 // FP32: the dequantized value exactly as a double-precision evaluation of the
 // definition rounds it ([P1] inverse of FP8量化 and of f).
-__device__ __forceinline__ float dequant_exact(uint32_t code, float scale, float k) {
+__device__ __forceinline__ float dequant_exact(uint32_t code, float scale, float k,
+                                              const double* coef) {
   const uint32_t mag = code & 0x7Fu;
   if (!(scale > 0.0f) || !(k > 0.0f) || mag == 0u) return 0.0f;
   const double a = kLog2TableD.v[mag] / (double)k;
-  const float x = (float)((double)scale * exp2_f64(a));
+  const float x = (float)((double)scale * exp2_f64(a, coef));
   return (code & 0x80u) ? -x : x;
 }
 
@@ -335,6 +333,7 @@ struct StepParams {
   float den_a;
   float den_b;
   float decay;         // 1 - lr * weight_decay
+  double exp2_coef[kExp2Terms];  // see exp2_f64
 };
 
 // Registers of one lane: 16 elements.
@@ -345,6 +344,27 @@ struct LaneData {
   uint32_t vc[4];
 };
 
+// Which elements a lane owns.  A group of G elements belongs to G/16
+// neighbouring lanes; inside the group the lanes interleave in runs of 4
+// elements: lane li of the group owns runs q = 0..3 at
+//   group_start + q * G/4 + 4 * li + (0..3),
+// so one memory instruction (fixed q) has each group's lanes covering G/4
+// consecutive elements: a w access is then G bytes of whole cache lines per
+// group, not one 16-byte piece per 64-byte segment.  Register j = 4q + r.
+template <int G>
+struct LaneMap {
+  static constexpr int kLanesPerGroup = G / kElemsPerLane;
+  static constexpr int kRunStride = G / 4;
+  int64_t grp;   // group index inside the tensor
+  int64_t base;  // element of register 0
+  __device__ __forceinline__ LaneMap(int64_t tile_start, int lane) {
+    grp = tile_start / G + lane / kLanesPerGroup;
+    base = grp * G + 4 * (lane % kLanesPerGroup);
+  }
+  __device__ __forceinline__ int64_t run(int q) const { return base + (int64_t)kRunStride * q; }
+  __device__ __forceinline__ int64_t elem(int j) const { return run(j >> 2) + (j & 3); }
+};
+
 constexpr int kExactRounds = 4;
 
 // Smallest nonzero |m_t| of the group as a key (2*bits - 2), evaluated
@@ -352,10 +372,11 @@ constexpr int kExactRounds = 4;
 // set to 0 in mt[] and skipped.  Returns a key >= kEmptyKey if the group has
 // no nonzero value.  `local` is this lane's indexed minimum key (see
 // Stats::add_indexed), `approx` the group's.  Control flow is wave-uniform.
-template <int kLanes>
-__device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, int64_t e0,
+template <int G>
+__device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, const LaneMap<G>& map,
                                                  const StepParams& p, float sm, float km,
                                                  uint32_t local, uint32_t approx, float (&mt)[16]) {
+  constexpr int kLanes = LaneMap<G>::kLanesPerGroup;
   uint32_t result = 0xFFFFFFFFu;
   bool done = approx >= kEmptyKey;
   uint32_t excluded = 0u;
@@ -363,9 +384,10 @@ __device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, int64_t
     uint32_t key = 0xFFFFFFFFu;
     if (!done && local == approx) {
       const uint32_t j = approx & 0xFu;
-      const uint32_t code = T.mc[e0 + j];
-      const float g = __uint_as_float((uint32_t)T.g[e0 + j] << 16);
-      const float m = moment_literal(p.b1, dequant_exact(code, sm, km), p.omb1, g);
+      const int64_t e = map.elem((int)j);
+      const uint32_t code = T.mc[e];
+      const float g = __uint_as_float((uint32_t)T.g[e] << 16);
+      const float m = moment_literal(p.b1, dequant_exact(code, sm, km, p.exp2_coef), p.omb1, g);
       if (m == 0.0f) {
         excluded |= 1u << j;
         key = 0xFFFFFFFEu;  // "exact zero" marker, above every real key
@@ -400,26 +422,23 @@ __device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, int64_t
   return result;
 }
 
-template <bool kFull>
-__device__ __forceinline__ void load_lane(const TensorDesc& T, int64_t e0, LaneData& L) {
+template <int G, bool kFull>
+__device__ __forceinline__ void load_lane(const TensorDesc& T, const LaneMap<G>& map, LaneData& L) {
   if constexpr (kFull) {
-    const float4* wp = reinterpret_cast<const float4*>(T.w + e0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 v = wp[q];
-      L.w[4 * q] = v.x;
-      L.w[4 * q + 1] = v.y;
-      L.w[4 * q + 2] = v.z;
-      L.w[4 * q + 3] = v.w;
+      const int64_t e = map.run(q);
+      const float4 w = *reinterpret_cast<const float4*>(T.w + e);
+      L.w[4 * q] = w.x;
+      L.w[4 * q + 1] = w.y;
+      L.w[4 * q + 2] = w.z;
+      L.w[4 * q + 3] = w.w;
+      const uint2 g = *reinterpret_cast<const uint2*>(T.g + e);
+      L.g[2 * q] = g.x;
+      L.g[2 * q + 1] = g.y;
+      L.mc[q] = *reinterpret_cast<const uint32_t*>(T.mc + e);
+      L.vc[q] = *reinterpret_cast<const uint32_t*>(T.vc + e);
     }
-    const uint4* gp = reinterpret_cast<const uint4*>(T.g + e0);
-    const uint4 g0 = gp[0], g1 = gp[1];
-    L.g[0] = g0.x; L.g[1] = g0.y; L.g[2] = g0.z; L.g[3] = g0.w;
-    L.g[4] = g1.x; L.g[5] = g1.y; L.g[6] = g1.z; L.g[7] = g1.w;
-    const uint4 m = *reinterpret_cast<const uint4*>(T.mc + e0);
-    const uint4 v = *reinterpret_cast<const uint4*>(T.vc + e0);
-    L.mc[0] = m.x; L.mc[1] = m.y; L.mc[2] = m.z; L.mc[3] = m.w;
-    L.vc[0] = v.x; L.vc[1] = v.y; L.vc[2] = v.z; L.vc[3] = v.w;
   } else {
     // Tail tile: element-wise, zero padding past n.  Zeros leave max|x| and
     // the nonzero minimum of a group unchanged.
@@ -430,7 +449,7 @@ __device__ __forceinline__ void load_lane(const TensorDesc& T, int64_t e0, LaneD
 #pragma unroll
     for (int j = 0; j < 4; ++j) { L.mc[j] = 0u; L.vc[j] = 0u; }
     for (int j = 0; j < 16; ++j) {
-      const int64_t e = e0 + j;
+      const int64_t e = map.elem(j);
       if (e < T.n) {
         L.w[j] = T.w[e];
         L.g[j >> 1] |= (uint32_t)T.g[e] << (16 * (j & 1));
@@ -441,28 +460,48 @@ __device__ __forceinline__ void load_lane(const TensorDesc& T, int64_t e0, LaneD
   }
 }
 
-template <bool kFull>
-__device__ __forceinline__ void store_codes(uint8_t* base, int64_t e0, int64_t n,
+template <int G, bool kFull>
+__device__ __forceinline__ void store_codes(uint8_t* base, const LaneMap<G>& map, int64_t n,
                                             const uint32_t (&c)[4]) {
   if constexpr (kFull) {
-    *reinterpret_cast<uint4*>(base + e0) = make_uint4(c[0], c[1], c[2], c[3]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(base + map.run(q)) = c[q];
   } else {
-    for (int j = 0; j < 16; ++j)
-      if (e0 + j < n) base[e0 + j] = (uint8_t)(c[j >> 2] >> (8 * (j & 3)));
+    for (int j = 0; j < 16; ++j) {
+      const int64_t e = map.elem(j);
+      if (e < n) base[e] = (uint8_t)(c[j >> 2] >> (8 * (j & 3)));
+    }
   }
 }
 
 template <int G, bool kFull>
-__device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t e0, int lane,
+__device__ __forceinline__ void store_floats(float* base, const LaneMap<G>& map, int64_t n,
+                                             const float (&x)[16]) {
+  if constexpr (kFull) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(base + map.run(q)) =
+          make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+  } else {
+    for (int j = 0; j < 16; ++j) {
+      const int64_t e = map.elem(j);
+      if (e < n) base[e] = x[j];
+    }
+  }
+}
+
+template <int G, bool kFull>
+__device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_start, int lane,
                                           const StepParams& p, const float2* tab) {
-  constexpr int kLanesPerGroup = G / kElemsPerLane;
-  const int64_t grp = e0 / G;
+  constexpr int kLanesPerGroup = LaneMap<G>::kLanesPerGroup;
+  const LaneMap<G> map(tile_start, lane);
+  const int64_t grp = map.grp;
   const int64_t ngroups = (T.n + G - 1) / G;
   const bool grp_ok = kFull || grp < ngroups;
 
   // a1: loads (all issued before any use)
   LaneData L;
-  load_lane<kFull>(T, e0, L);
+  load_lane<G, kFull>(T, map, L);
   float sm = 0.0f, km = 0.0f, sv = 0.0f, kv = 0.0f;
   if (grp_ok) {
     sm = T.ms[grp];
@@ -470,6 +509,7 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t e0, int l
     sv = T.vs[grp];
     kv = T.vk[grp];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load of the tile in flight together
 
   // a2: dequantize-expand both moments
   const DequantConst dm = dequant_const(sm, km);
@@ -497,63 +537,65 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t e0, int l
     st_m.add_indexed(m, (uint32_t)j);
     st_v.add(v);
   }
-  if constexpr (kFull) {
-    float4* wp = reinterpret_cast<float4*>(T.w + e0);
+  store_floats<G, kFull>(T.w, map, T.n, L.w);
+
+  // a5-a7 for the second moment first, so its registers are free for the
+  // first moment's exact minimum below.
+  {
+    const uint32_t v_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_v.max_abs));
+    const uint32_t v_min = group_min_u32<kLanesPerGroup>(st_v.min_key);
+    const QuantConst qv = quant_const(v_max, v_min);
+    uint32_t ov[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      wp[q] = make_float4(L.w[4 * q], L.w[4 * q + 1], L.w[4 * q + 2], L.w[4 * q + 3]);
-  } else {
-    for (int j = 0; j < 16; ++j)
-      if (e0 + j < T.n) T.w[e0 + j] = L.w[j];
+      ov[q] = pack4(quant_mag(vt[4 * q], qv), quant_mag(vt[4 * q + 1], qv),
+                    quant_mag(vt[4 * q + 2], qv), quant_mag(vt[4 * q + 3], qv));
+    store_codes<G, kFull>(T.vc, map, T.n, ov);
+    if ((lane % kLanesPerGroup) == 0 && grp_ok) {
+      T.vs[grp] = qv.scale;
+      T.vk[grp] = qv.k;
+    }
   }
 
-  // a5: group statistics across the group's lanes
+  // a5: first-moment group statistics across the group's lanes.  Its
+  // smallest nonzero magnitude sets k, and it is usually the element where
+  // b1*m and (1-b1)*g cancel most, so an FP32 rounding difference in its
+  // dequantized m is magnified there: the lane holding the group's FP32
+  // minimum re-evaluates that one element exactly as the definition rounds it
+  // (see exact_group_min).
   const uint32_t m_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_m.max_abs));
   const uint32_t m_min_approx = group_min_u32<kLanesPerGroup>(st_m.min_key);
-  const uint32_t v_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_v.max_abs));
-  const uint32_t v_min = group_min_u32<kLanesPerGroup>(st_v.min_key);
+  const uint32_t m_min = exact_group_min<G>(T, map, p, sm, km, st_m.min_key, m_min_approx, mt);
 
-  // The first moment's smallest nonzero magnitude sets k, and it is usually
-  // the element where b1*m and (1-b1)*g cancel most, so an FP32 rounding
-  // difference in its dequantized m is magnified there.  The lane holding
-  // the group's FP32 minimum re-evaluates that one element exactly as the
-  // definition rounds it (dequantization in double rounded once, then the
-  // literal AdamW moment update).  If that value is exactly zero, the
-  // element is a zero, not the minimum: it is excluded and the next smallest
-  // element is tried (a few rounds, decided per wave).
-  const uint32_t m_min = exact_group_min<kLanesPerGroup>(T, e0, p, sm, km, st_m.min_key,
-                                                        m_min_approx, mt);
-
-  // a6: expansion exponent and scale per group (a group whose only nonzero
-  // first-moment values are exact zeros is empty)
+  // a6: expansion exponent and scale (a group whose only nonzero values are
+  // exact zeros is empty)
   const QuantConst qm = quant_const(m_min < kEmptyKey ? m_max : 0u, m_min);
-  const QuantConst qv = quant_const(v_max, v_min);
 
   // a7: expand, scale, round, pack, store
-  uint32_t om[4], ov[4];
+  uint32_t om[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float a[4], b[4];
+    float a[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float x = mt[4 * q + r];
       a[r] = copysignf(quant_mag(x, qm), x);
-      b[r] = quant_mag(vt[4 * q + r], qv);
     }
     om[q] = pack4(a[0], a[1], a[2], a[3]);
-    ov[q] = pack4(b[0], b[1], b[2], b[3]);
   }
-  store_codes<kFull>(T.mc, e0, T.n, om);
-  store_codes<kFull>(T.vc, e0, T.n, ov);
+  store_codes<G, kFull>(T.mc, map, T.n, om);
   if ((lane % kLanesPerGroup) == 0 && grp_ok) {
     T.ms[grp] = qm.scale;
     T.mk[grp] = qm.k;
-    T.vs[grp] = qv.scale;
-    T.vk[grp] = qv.k;
   }
 }
 
-template <int G>
+// kTail = false: the full tiles of every tensor of the launch (the streaming
+// kernel).  kTail = true: the one partial last tile of each tensor whose size
+// is not a multiple of the tile (tile_end then counts 0 or 1 per tensor).
+// The two are separate kernels so that the rarely used element-wise tail code
+// does not set the register budget, and so the occupancy, of the main one.
+template <int G, bool kTail>
 __global__ __launch_bounds__(kBlockThreads) void adamw_fp8_step_kernel(const StepParams p) {
   __shared__ float2 tab[256];
   load_log2_table(tab);
@@ -569,12 +611,10 @@ __global__ __launch_bounds__(kBlockThreads) void adamw_fp8_step_kernel(const Ste
       ++ti;
     }
     const TensorDesc& T = p.t[ti];
-    const int64_t local = tile - tile_begin;
-    const int64_t e0 = local * kTileElems + (int64_t)lane * kElemsPerLane;
-    if ((local + 1) * kTileElems <= T.n)
-      step_lane<G, true>(T, e0, lane, p, tab);
+    if constexpr (!kTail)
+      step_lane<G, true>(T, (tile - tile_begin) * kTileElems, lane, p, tab);
     else
-      step_lane<G, false>(T, e0, lane, p, tab);
+      step_lane<G, false>(T, T.n / kTileElems * kTileElems, lane, p, tab);
   }
 }
 
@@ -590,24 +630,26 @@ struct CodecParams {
   const float* scale_in;
   const float* k_in;
   int64_t n;
-  int64_t tiles;
 };
 
 template <int G, bool kFull>
-__device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t e0, int lane) {
-  constexpr int kLanesPerGroup = G / kElemsPerLane;
-  const int64_t grp = e0 / G;
+__device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t tile_start, int lane) {
+  constexpr int kLanesPerGroup = LaneMap<G>::kLanesPerGroup;
+  const LaneMap<G> map(tile_start, lane);
+  const int64_t grp = map.grp;
   const bool grp_ok = kFull || grp < (p.n + G - 1) / G;
   float x[16];
   if constexpr (kFull) {
-    const float4* xp = reinterpret_cast<const float4*>(p.x + e0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 v = xp[q];
+      const float4 v = *reinterpret_cast<const float4*>(p.x + map.run(q));
       x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
     }
   } else {
-    for (int j = 0; j < 16; ++j) x[j] = (e0 + j < p.n) ? p.x[e0 + j] : 0.0f;
+    for (int j = 0; j < 16; ++j) {
+      const int64_t e = map.elem(j);
+      x[j] = (e < p.n) ? p.x[e] : 0.0f;
+    }
   }
   Stats st;
 #pragma unroll
@@ -622,7 +664,7 @@ __device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t e0, 
     for (int r = 0; r < 4; ++r) a[r] = copysignf(quant_mag(x[4 * q + r], qc), x[4 * q + r]);
     o[q] = pack4(a[0], a[1], a[2], a[3]);
   }
-  store_codes<kFull>(p.codes, e0, p.n, o);
+  store_codes<G, kFull>(p.codes, map, p.n, o);
   if ((lane % kLanesPerGroup) == 0 && grp_ok) {
     p.scale[grp] = qc.scale;
     p.k[grp] = qc.k;
@@ -630,17 +672,20 @@ __device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t e0, 
 }
 
 template <int G, bool kFull>
-__device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t e0,
+__device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t tile_start, int lane,
                                                 const float2* tab) {
-  const int64_t grp = e0 / G;
+  const LaneMap<G> map(tile_start, lane);
+  const int64_t grp = map.grp;
   const bool grp_ok = kFull || grp < (p.n + G - 1) / G;
   uint32_t c[4] = {0u, 0u, 0u, 0u};
   if constexpr (kFull) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p.codes_in + e0);
-    c[0] = v.x; c[1] = v.y; c[2] = v.z; c[3] = v.w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const uint32_t*>(p.codes_in + map.run(q));
   } else {
-    for (int j = 0; j < 16; ++j)
-      if (e0 + j < p.n) c[j >> 2] |= (uint32_t)p.codes_in[e0 + j] << (8 * (j & 3));
+    for (int j = 0; j < 16; ++j) {
+      const int64_t e = map.elem(j);
+      if (e < p.n) c[j >> 2] |= (uint32_t)p.codes_in[e] << (8 * (j & 3));
+    }
   }
   const DequantConst d = dequant_const(grp_ok ? p.scale_in[grp] : 0.0f,
                                        grp_ok ? p.k_in[grp] : 0.0f);
@@ -650,18 +695,12 @@ __device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t e0
     const float2 e = tab[(c[j >> 2] >> (8 * (j & 3))) & 0xFF];
     x[j] = dequant_mag(e.x, d) * e.y;
   }
-  if constexpr (kFull) {
-    float4* xp = reinterpret_cast<float4*>(p.xo + e0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      xp[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
-  } else {
-    for (int j = 0; j < 16; ++j)
-      if (e0 + j < p.n) p.xo[e0 + j] = x[j];
-  }
+  store_floats<G, kFull>(p.xo, map, p.n, x);
 }
 
-template <int G, bool kQuantize>
+// Same split as the step: kTail = false walks the full tiles, kTail = true
+// handles the single partial last tile.
+template <int G, bool kQuantize, bool kTail>
 __global__ __launch_bounds__(kBlockThreads) void codec_kernel(const CodecParams p) {
   __shared__ float2 tab[256];
   if constexpr (!kQuantize) load_log2_table(tab);
@@ -669,16 +708,13 @@ __global__ __launch_bounds__(kBlockThreads) void codec_kernel(const CodecParams 
   const int64_t wave =
       (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t tile = wave; tile < p.tiles; tile += nwaves) {
-    const int64_t e0 = tile * kTileElems + (int64_t)lane * kElemsPerLane;
-    const bool full = (tile + 1) * kTileElems <= p.n;
-    if constexpr (kQuantize) {
-      if (full) quantize_lane<G, true>(p, e0, lane);
-      else quantize_lane<G, false>(p, e0, lane);
-    } else {
-      if (full) dequantize_lane<G, true>(p, e0, tab);
-      else dequantize_lane<G, false>(p, e0, tab);
-    }
+  const int64_t tiles = kTail ? 1 : p.n / kTileElems;
+  for (int64_t tile = wave; tile < tiles; tile += nwaves) {
+    const int64_t tile_start = kTail ? p.n / kTileElems * kTileElems : tile * kTileElems;
+    if constexpr (kQuantize)
+      quantize_lane<G, !kTail>(p, tile_start, lane);
+    else
+      dequantize_lane<G, !kTail>(p, tile_start, lane, tab);
   }
 }
 
@@ -765,26 +801,33 @@ hipError_t launch_persistent(const void* fn, int64_t tiles, void* arg, hipStream
 }
 
 template <int G>
-const void* step_fn() {
-  return reinterpret_cast<const void*>(&adamw_fp8_step_kernel<G>);
+const void* step_fn(bool tail) {
+  return tail ? reinterpret_cast<const void*>(&adamw_fp8_step_kernel<G, true>)
+              : reinterpret_cast<const void*>(&adamw_fp8_step_kernel<G, false>);
 }
 
-const void* step_kernel_for(int32_t g) {
+const void* step_kernel_for(int32_t g, bool tail) {
   switch (g) {
-    case 16: return step_fn<16>();
-    case 32: return step_fn<32>();
-    case 64: return step_fn<64>();
-    default: return step_fn<128>();
+    case 16: return step_fn<16>(tail);
+    case 32: return step_fn<32>(tail);
+    case 64: return step_fn<64>(tail);
+    default: return step_fn<128>(tail);
   }
 }
 
+template <int G, bool kQuantize>
+const void* codec_fn(bool tail) {
+  return tail ? reinterpret_cast<const void*>(&codec_kernel<G, kQuantize, true>)
+              : reinterpret_cast<const void*>(&codec_kernel<G, kQuantize, false>);
+}
+
 template <bool kQuantize>
-const void* codec_kernel_for(int32_t g) {
+const void* codec_kernel_for(int32_t g, bool tail) {
   switch (g) {
-    case 16: return reinterpret_cast<const void*>(&codec_kernel<16, kQuantize>);
-    case 32: return reinterpret_cast<const void*>(&codec_kernel<32, kQuantize>);
-    case 64: return reinterpret_cast<const void*>(&codec_kernel<64, kQuantize>);
-    default: return reinterpret_cast<const void*>(&codec_kernel<128, kQuantize>);
+    case 16: return codec_fn<16, kQuantize>(tail);
+    case 32: return codec_fn<32, kQuantize>(tail);
+    case 64: return codec_fn<64, kQuantize>(tail);
+    default: return codec_fn<128, kQuantize>(tail);
   }
 }
 
@@ -794,7 +837,41 @@ coat_status_t check_state(const coat_fp8_state_t& s) {
   return COAT_OK;
 }
 
-int64_t tiles_of(int64_t n) { return (n + kTileElems - 1) / kTileElems; }
+// Launches the full-tile kernel over the first `used` descriptors of p, then
+// the tail kernel over the tensors that end in a partial tile.
+hipError_t launch_step(StepParams& p, int used, int32_t group_size, hipStream_t stream) {
+  int64_t full = 0, tails = 0;
+  for (int i = 0; i < used; ++i) {
+    full += p.t[i].n / kTileElems;
+    p.t[i].tile_end = full;
+  }
+  p.total_tiles = full;
+  if (full > 0) {
+    const hipError_t e = launch_persistent(step_kernel_for(group_size, false), full, &p, stream);
+    if (e != hipSuccess) return e;
+  }
+  for (int i = 0; i < used; ++i) {
+    tails += (p.t[i].n % kTileElems) ? 1 : 0;
+    p.t[i].tile_end = tails;
+  }
+  p.total_tiles = tails;
+  if (tails > 0) return launch_persistent(step_kernel_for(group_size, true), tails, &p, stream);
+  return hipSuccess;
+}
+
+template <bool kQuantize>
+hipError_t launch_codec(const CodecParams& p, int32_t group_size, hipStream_t stream) {
+  CodecParams q = p;
+  const int64_t full = p.n / kTileElems;
+  if (full > 0) {
+    const hipError_t e =
+        launch_persistent(codec_kernel_for<kQuantize>(group_size, false), full, &q, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (p.n % kTileElems)
+    return launch_persistent(codec_kernel_for<kQuantize>(group_size, true), 1, &q, stream);
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -839,10 +916,9 @@ coat_status_t coat_adamw_fp8_step(const coat_adamw_tensor_t* tensors, int32_t nu
     p.den_b = INFINITY;
   }
   p.decay = (float)(1.0 - (double)hp->lr * (double)hp->weight_decay);
+  exp2_coefficients(p.exp2_coef);
 
-  const void* fn = step_kernel_for(hp->group_size);
   int used = 0;
-  int64_t tiles = 0;
   for (int32_t i = 0; i < num_tensors; ++i) {
     const coat_adamw_tensor_t& t = tensors[i];
     if (t.n == 0) continue;
@@ -856,20 +932,15 @@ coat_status_t coat_adamw_fp8_step(const coat_adamw_tensor_t* tensors, int32_t nu
     d.vs = t.v.scale;
     d.vk = t.v.k;
     d.n = t.n;
-    tiles += tiles_of(t.n);
-    d.tile_end = tiles;
     if (used == kMaxTensorsPerLaunch) {
-      p.total_tiles = tiles;
-      const hipError_t e = launch_persistent(fn, tiles, &p, stream);
+      const hipError_t e = launch_step(p, used, hp->group_size, stream);
       if (e != hipSuccess) return hip_fail(e);
       used = 0;
-      tiles = 0;
     }
   }
   if (used > 0) {
-    p.total_tiles = tiles;
     // descriptors past `used` are never reached: tile < total_tiles
-    const hipError_t e = launch_persistent(fn, tiles, &p, stream);
+    const hipError_t e = launch_step(p, used, hp->group_size, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
   return COAT_OK;
@@ -891,8 +962,7 @@ coat_status_t coat_fp8_expand_quantize(const float* x, int64_t n, int32_t group_
   p.scale = out.scale;
   p.k = out.k;
   p.n = n;
-  p.tiles = tiles_of(n);
-  const hipError_t e = launch_persistent(codec_kernel_for<true>(group_size), p.tiles, &p, stream);
+  const hipError_t e = launch_codec<true>(p, group_size, stream);
   return e == hipSuccess ? COAT_OK : hip_fail(e);
 }
 
@@ -912,8 +982,7 @@ coat_status_t coat_fp8_dequantize_expand(const uint8_t* codes, const float* scal
   p.k_in = k;
   p.xo = x;
   p.n = n;
-  p.tiles = tiles_of(n);
-  const hipError_t e = launch_persistent(codec_kernel_for<false>(group_size), p.tiles, &p, stream);
+  const hipError_t e = launch_codec<false>(p, group_size, stream);
   return e == hipSuccess ? COAT_OK : hip_fail(e);
 }
 

@@ -15,9 +15,9 @@
 // of G elements lives in G/16 neighbouring lanes and its max / min reductions
 // are 0..3 DPP steps inside registers (see LaneMap for the interleave that
 // keeps every memory instruction on whole cache lines).  LDS holds only a
-// 2 KB table for dequantization.  Waves walk the tiles of all tensors of one
-// launch with a grid stride; tensor descriptors travel in the kernel
-// arguments.
+// 2 KB table for dequantization.  Each wave takes one tile, found by a
+// binary search over the launch's tensors, whose descriptors travel in the
+// kernel arguments.
 
 #include <hip/hip_runtime.h>
 
@@ -26,8 +26,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
-#include <vector>
 
 #include "coat_fp8.h"
 
@@ -603,14 +601,16 @@ __global__ __launch_bounds__(kBlockThreads) void adamw_fp8_step_kernel(const Ste
   const int64_t wave =
       (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  int ti = 0;
-  int64_t tile_begin = 0;
   for (int64_t tile = wave; tile < p.total_tiles; tile += nwaves) {
-    while (tile >= p.t[ti].tile_end) {  // wave-uniform, monotone
-      tile_begin = p.t[ti].tile_end;
-      ++ti;
+    // first tensor whose cumulative tile count exceeds `tile` (entries past
+    // the launch's tensors hold INT64_MAX, so the array is monotone)
+    int lo = 0, hi = kMaxTensorsPerLaunch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (tile < p.t[mid].tile_end) hi = mid; else lo = mid + 1;
     }
-    const TensorDesc& T = p.t[ti];
+    const int64_t tile_begin = lo > 0 ? p.t[lo - 1].tile_end : 0;
+    const TensorDesc& T = p.t[lo];
     if constexpr (!kTail)
       step_lane<G, true>(T, (tile - tile_begin) * kTileElems, lane, p, tab);
     else
@@ -750,52 +750,13 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool valid_group_size(int32_t g) { return g == 16 || g == 32 || g == 64 || g == 128; }
 
-// Resident-block capacity of a kernel on the current device: the persistent
-// grid never exceeds it, so no block waits behind another's whole loop.
-struct LaunchShape {
-  int blocks_per_cu = 0;
-  int cus = 0;
-};
-
-std::mutex g_shape_mu;
-struct ShapeKey {
-  int device;
-  const void* fn;
-  LaunchShape shape;
-};
-std::vector<ShapeKey> g_shapes;
-
-hipError_t launch_shape(const void* fn, LaunchShape* out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  {
-    std::lock_guard<std::mutex> lk(g_shape_mu);
-    for (const ShapeKey& s : g_shapes)
-      if (s.device == dev && s.fn == fn) {
-        *out = s.shape;
-        return hipSuccess;
-      }
-  }
-  LaunchShape sh;
-  e = hipDeviceGetAttribute(&sh.cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&sh.blocks_per_cu, fn, kBlockThreads, 0);
-  if (e != hipSuccess) return e;
-  if (sh.blocks_per_cu < 1) sh.blocks_per_cu = 1;
-  std::lock_guard<std::mutex> lk(g_shape_mu);
-  g_shapes.push_back({dev, fn, sh});
-  *out = sh;
-  return hipSuccess;
-}
-
-hipError_t launch_persistent(const void* fn, int64_t tiles, void* arg, hipStream_t stream) {
-  LaunchShape sh;
-  hipError_t e = launch_shape(fn, &sh);
-  if (e != hipSuccess) return e;
+// One wave per tile: the grid covers every tile once (the grid-stride loops
+// in the kernels then run one iteration).  Measured on MI355X, this streams
+// faster than a grid sized to the resident capacity that loops over tiles:
+// the dispatcher keeps handing fresh tiles to whichever CU frees up.
+hipError_t launch_tiles(const void* fn, int64_t tiles, void* arg, hipStream_t stream) {
   const int64_t want = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  const int64_t cap = (int64_t)sh.cus * sh.blocks_per_cu;
-  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min(want, cap));
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(want, 0x7FFFFFFF));
   void* args[] = {arg};
   return hipLaunchKernel(fn, dim3(blocks), dim3(kBlockThreads), args, 0, stream);
 }
@@ -845,17 +806,19 @@ hipError_t launch_step(StepParams& p, int used, int32_t group_size, hipStream_t 
     full += p.t[i].n / kTileElems;
     p.t[i].tile_end = full;
   }
+  for (int i = used; i < kMaxTensorsPerLaunch; ++i) p.t[i].tile_end = INT64_MAX;
   p.total_tiles = full;
   if (full > 0) {
-    const hipError_t e = launch_persistent(step_kernel_for(group_size, false), full, &p, stream);
+    const hipError_t e = launch_tiles(step_kernel_for(group_size, false), full, &p, stream);
     if (e != hipSuccess) return e;
   }
   for (int i = 0; i < used; ++i) {
     tails += (p.t[i].n % kTileElems) ? 1 : 0;
     p.t[i].tile_end = tails;
   }
+  for (int i = used; i < kMaxTensorsPerLaunch; ++i) p.t[i].tile_end = INT64_MAX;
   p.total_tiles = tails;
-  if (tails > 0) return launch_persistent(step_kernel_for(group_size, true), tails, &p, stream);
+  if (tails > 0) return launch_tiles(step_kernel_for(group_size, true), tails, &p, stream);
   return hipSuccess;
 }
 
@@ -865,11 +828,11 @@ hipError_t launch_codec(const CodecParams& p, int32_t group_size, hipStream_t st
   const int64_t full = p.n / kTileElems;
   if (full > 0) {
     const hipError_t e =
-        launch_persistent(codec_kernel_for<kQuantize>(group_size, false), full, &q, stream);
+        launch_tiles(codec_kernel_for<kQuantize>(group_size, false), full, &q, stream);
     if (e != hipSuccess) return e;
   }
   if (p.n % kTileElems)
-    return launch_persistent(codec_kernel_for<kQuantize>(group_size, true), 1, &q, stream);
+    return launch_tiles(codec_kernel_for<kQuantize>(group_size, true), 1, &q, stream);
   return hipSuccess;
 }
 

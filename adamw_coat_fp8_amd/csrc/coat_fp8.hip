@@ -371,9 +371,9 @@ constexpr int kExactRounds = 4;
 // no nonzero value.  `local` is this lane's indexed minimum key (see
 // Stats::add_indexed), `approx` the group's.  Control flow is wave-uniform.
 template <int G>
-__device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, const LaneMap<G>& map,
-                                                 const StepParams& p, float sm, float km,
-                                                 uint32_t local, uint32_t approx, float (&mt)[16]) {
+__device__ __forceinline__ uint32_t exact_group_min(const LaneData& L, const StepParams& p,
+                                                 float sm, float km, uint32_t local,
+                                                 uint32_t approx, float (&mt)[16]) {
   constexpr int kLanes = LaneMap<G>::kLanesPerGroup;
   uint32_t result = 0xFFFFFFFFu;
   bool done = approx >= kEmptyKey;
@@ -382,9 +382,14 @@ __device__ __forceinline__ uint32_t exact_group_min(const TensorDesc& T, const L
     uint32_t key = 0xFFFFFFFFu;
     if (!done && local == approx) {
       const uint32_t j = approx & 0xFu;
-      const int64_t e = map.elem((int)j);
-      const uint32_t code = T.mc[e];
-      const float g = __uint_as_float((uint32_t)T.g[e] << 16);
+      // the element's code byte and BF16 gradient, picked from registers
+      uint32_t cw = L.mc[0], gw = L.g[0];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) cw = ((j >> 2) == (uint32_t)q) ? L.mc[q] : cw;
+#pragma unroll
+      for (int h = 1; h < 8; ++h) gw = ((j >> 1) == (uint32_t)h) ? L.g[h] : gw;
+      const uint32_t code = (cw >> (8 * (j & 3u))) & 0xFFu;
+      const float g = __uint_as_float((j & 1u) ? (gw & 0xFFFF0000u) : (gw << 16));
       const float m = moment_literal(p.b1, dequant_exact(code, sm, km, p.exp2_coef), p.omb1, g);
       if (m == 0.0f) {
         excluded |= 1u << j;
@@ -563,7 +568,7 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
   // (see exact_group_min).
   const uint32_t m_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_m.max_abs));
   const uint32_t m_min_approx = group_min_u32<kLanesPerGroup>(st_m.min_key);
-  const uint32_t m_min = exact_group_min<G>(T, map, p, sm, km, st_m.min_key, m_min_approx, mt);
+  const uint32_t m_min = exact_group_min<G>(L, p, sm, km, st_m.min_key, m_min_approx, mt);
 
   // a6: expansion exponent and scale (a group whose only nonzero values are
   // exact zeros is empty)

@@ -1,0 +1,98 @@
+"""Host-side logic that runs without a GPU: workload shapes, the flat shard
+layout, the split of a tensor list into library calls, the benchmark's byte
+accounting and its refusal of multi-GPU runs, and the stress input recipe."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from adamw_coat_fp8_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("name,tensors,params", [
+    ("single_1m", 1, 1_048_576),
+    ("olmo_1b", 146, 1_176_832_000),
+    ("llama2_7b", 291, 6_738_415_616),
+    ("llama2_13b", 363, 13_015_864_320),
+])
+def test_workload_shapes(name, tensors, params):
+    specs = inputs.workload_specs(name)
+    assert len(specs) == tensors
+    assert inputs.total_params(specs) == params
+    # every tensor of these shapes is a whole number of 128-element groups
+    assert all(s.numel % 128 == 0 for s in specs)
+
+
+def test_balanced_calls_cover_list_within_launch_capacity():
+    from adamw_coat_fp8_amd.shard import MAX_TENSORS_PER_CALL, balanced_calls
+    for name in ("olmo_1b", "llama2_7b", "llama2_13b"):
+        numels = [s.numel for s in inputs.workload_specs(name)]
+        calls = balanced_calls(numels)
+        flat = [i for c in calls for i in c]
+        assert flat == list(range(len(numels)))          # contiguous, in order
+        assert all(1 <= len(c) <= MAX_TENSORS_PER_CALL for c in calls)
+        sizes = [sum(numels[i] for i in c) for c in calls]
+        assert max(sizes) <= 1.3 * sum(numels) / len(calls)
+    rng = np.random.default_rng(0)
+    numels = [int(x) for x in rng.integers(1, 10_000, 500)]
+    calls = balanced_calls(numels)
+    assert [i for c in calls for i in c] == list(range(500))
+    assert all(len(c) <= MAX_TENSORS_PER_CALL for c in calls)
+
+
+def test_flat_shard_layout_alignment():
+    from adamw_coat_fp8_amd.shard import FP8AdamWShard
+    numels = [1000, 1, 17, 4096, 4101, 128 * 3]
+    for G in (16, 32, 64, 128):
+        sh = FP8AdamWShard(numels, group_size=G, device="cpu")
+        for i, n in enumerate(numels):
+            slot = sh.slots[i]
+            assert slot.w.numel() == n and slot.grad.numel() == n
+            assert slot.m.codes.numel() == n and slot.v.codes.numel() == n
+            assert slot.m.scale.numel() == -(-n // G) == slot.v.k.numel()
+            for t in (slot.w, slot.grad, slot.m.codes, slot.v.codes):
+                assert t.data_ptr() % 16 == 0
+            for t in (slot.m.scale, slot.m.k, slot.v.scale, slot.v.k):
+                assert t.data_ptr() % 4 == 0
+        # views do not overlap
+        ends = [(sh.offsets[i], sh.offsets[i] + n) for i, n in enumerate(numels)]
+        assert all(a[1] <= b[0] for a, b in zip(ends, ends[1:]))
+        assert sh.state_bytes() == 2 * sh.total_elems + 16 * sh.total_groups
+
+
+def test_bench_byte_accounting():
+    sys.path.insert(0, ROOT)
+    import bench
+    numels = [s.numel for s in inputs.workload_specs("llama2_7b")]
+    total = sum(bench.algorithmic_bytes(n, 128) for n in numels)
+    # 14 B per parameter and 32 B per 128-element group
+    assert total == 14 * 6_738_415_616 + 32 * 52_643_872 == 96_022_422_528
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_stress_recipe_features():
+    n, G = 128 * 400 + 77, 128
+    g = inputs.gradient(n, 1e-3, 1, 0, "cpu", kind="stress", group_size=G).float().numpy()
+    g2 = inputs.gradient(n, 1e-3, 2, 0, "cpu", kind="stress", group_size=G).float().numpy()
+    zero1, zero2 = g == 0, g2 == 0
+    assert 0.05 < zero1.mean() < 0.15               # 5% mask plus zeroed groups
+    zero3 = inputs.gradient(n, 1e-3, 3, 0, "cpu", kind="stress", group_size=G).float().numpy() == 0
+    # the exact-zero mask is the same on every step (plus the all-zero groups)
+    assert (zero1 & zero2 & zero3).mean() > 0.05
+    assert np.array_equal(zero1 & zero2, zero1 & zero2 & zero3)
+    groups = np.split(g, np.arange(G, n, G))
+    nnz = np.array([np.count_nonzero(x) for x in groups])
+    assert (nnz == 1).any() and (nnz == 0).any()     # single-nonzero and all-zero groups
+    assert np.any(np.isclose(np.abs(g), 4.5e-15, rtol=0.01))   # tiny magnitudes
+    assert inputs.gradient(n, 1e-3, 1, 0, "cpu", kind="stress", group_size=G).dtype == torch.bfloat16

@@ -54,6 +54,9 @@ def _lib():
             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
             ctypes.c_float, ctypes.c_int64, _vp, _vp, _vp, _vp]
+        lib.coat_oracle_quantize_act.restype = ctypes.c_int
+        lib.coat_oracle_quantize_act.argtypes = [
+            _u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _u8p, _f32p, _vp]
         _LIB = lib
     return _LIB
 
@@ -163,3 +166,18 @@ def adamw_fp8_step(w, g_bf16, m, v, group_size, lr, beta1, beta2, eps,
         _ptr(out.get("m_t")), _ptr(out.get("v_t")),
         _ptr(out.get("q_m")), _ptr(out.get("q_v"))), "adamw_fp8_step")
     return out
+
+
+def quantize_act(x_bf16_bits, rows, cols, group_size, transpose=True):
+    """Per-group (1 x group_size) E4M3 quantization of a row-major BF16 matrix
+    given as uint16 bit patterns.  Returns (codes[rows, cols],
+    scales[rows, cols // group_size], codes_t[cols, rows] or None)."""
+    x = np.ascontiguousarray(x_bf16_bits, dtype=np.uint16).ravel()
+    assert x.size == rows * cols
+    codes = np.zeros(rows * cols, np.uint8)
+    scales = np.zeros(rows * (cols // group_size), np.float32)
+    codes_t = np.zeros(rows * cols, np.uint8) if transpose else None
+    _check(_lib().coat_oracle_quantize_act(x, rows, cols, group_size, codes, scales,
+                                           _ptr(codes_t)), "quantize_act")
+    return (codes.reshape(rows, cols), scales.reshape(rows, cols // group_size),
+            None if codes_t is None else codes_t.reshape(cols, rows))

@@ -303,3 +303,40 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
   free(vg);
   return rc;
 }
+
+/* --------------------------------------------- activation quantizer (1xG) */
+
+/* [P1] eq. FP8量化 on each 1xG group of a row: S = max|X| / 448 and
+ * X_FP8 = round(X / S), evaluated as x * (448 / max) in FP32. */
+int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                             int32_t group_size, uint8_t* codes, float* scales,
+                             uint8_t* codes_t) {
+  if (rows < 0 || cols < 0 || group_size < 1 || cols % group_size != 0)
+    return COAT_ORACLE_EINVAL;
+  const int64_t groups_per_row = cols / group_size;
+  for (int64_t i = 0; i < rows; ++i) {
+    for (int64_t gj = 0; gj < groups_per_row; ++gj) {
+      const int64_t c0 = gj * group_size;
+      float amax = 0.0f;
+      for (int64_t j = c0; j < c0 + group_size; ++j) {
+        const float a = fabsf(bf16_to_float(x_bf16[i * cols + j]));
+        if (a > amax) amax = a;
+      }
+      if (amax == 0.0f) {
+        scales[i * groups_per_row + gj] = 0.0f;
+        for (int64_t j = c0; j < c0 + group_size; ++j) codes[i * cols + j] = 0x00;
+        continue;
+      }
+      const float r = (float)kE4M3Max / amax;
+      scales[i * groups_per_row + gj] = amax / (float)kE4M3Max;
+      for (int64_t j = c0; j < c0 + group_size; ++j) {
+        const float q = bf16_to_float(x_bf16[i * cols + j]) * r;
+        codes[i * cols + j] = coat_oracle_e4m3_encode((double)q);
+      }
+    }
+  }
+  if (codes_t)
+    for (int64_t i = 0; i < rows; ++i)
+      for (int64_t j = 0; j < cols; ++j) codes_t[j * rows + i] = codes[i * cols + j];
+  return COAT_ORACLE_OK;
+}

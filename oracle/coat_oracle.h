@@ -91,6 +91,19 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
                                float* m_out, float* v_out,
                                double* qm_out, double* qv_out);
 
+/* Per-group E4M3 quantization of a row-major BF16 activation matrix
+ * ([P1] section 三 "混合粒度激活量化": 1xG groups for non-linear layers, and the
+ * non-linear-layer kernel's quantized output plus transposed quantized output;
+ * [P1] eq. FP8量化 with S = max|X| / 448 per group).  Reading: the rounding
+ * decision is taken in FP32, r = 448 / max (IEEE division), code =
+ * RNE(x * r); the stored scale is S = max / 448 (IEEE division); an all-zero
+ * group stores S = 0 and codes 0.  cols must be a multiple of group_size.
+ * codes: rows x cols, scales: rows x cols/group_size, codes_t: cols x rows
+ * (the transpose of codes; may be NULL). */
+int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
+                             int32_t group_size, uint8_t* codes, float* scales,
+                             uint8_t* codes_t);
+
 #ifdef __cplusplus
 }
 #endif

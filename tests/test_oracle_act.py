@@ -1,0 +1,116 @@
+"""Pins of the oracle's per-group (1 x G) activation quantizer (COAT review,
+section 三 "混合粒度激活量化" and eq. FP8量化; transposed FP8 output of the
+non-linear-layer kernels).
+
+Pinned by: torch's FP8 cast on the FP32 products (library), exact power-of-two
+groups (closed form), the format's round-trip error bound, degenerate groups,
+the transpose relation, the memory-overhead row the page prints (golden), and
+the direction of the mixed-granularity claim (per-group error below
+per-tensor error on activations with outliers)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "act_group_overhead.json")
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _act(rows, cols, seed, outliers=True):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(rows, cols, generator=g)
+    if outliers:  # a few large channels, as in transformer activations
+        ch = torch.randint(0, cols, (max(1, cols // 64),), generator=g)
+        x[:, ch] *= 50.0
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+def test_matches_torch_cast_of_fp32_products(G):
+    rows, cols = 37, 4 * G
+    x = _act(rows, cols, G)
+    codes, scales, codes_t = oracle.quantize_act(_bits(x), rows, cols, G)
+    xf = x.float().reshape(rows, cols // G, G)
+    amax = xf.abs().amax(-1, keepdim=True)
+    r = torch.tensor(448.0, dtype=torch.float32) / amax          # IEEE FP32 division
+    ref = (xf * r).reshape(rows, cols).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    assert np.array_equal(scales, (amax / 448.0).reshape(rows, cols // G).numpy())
+    assert np.array_equal(codes_t, codes.T)
+
+
+def test_power_of_two_group_closed_form():
+    G = 16
+    m = 3.0 * 2.0 ** -7
+    vals = np.array([m * 2.0 ** -j for j in range(G)], np.float32)
+    vals[1::2] *= -1
+    x = torch.from_numpy(vals).reshape(1, G).to(torch.bfloat16)
+    assert np.array_equal(x.float().numpy().ravel(), vals)        # exact in BF16
+    codes, scales, _ = oracle.quantize_act(_bits(x), 1, G, G)
+    assert scales[0, 0] == np.float32(m / 448.0)
+    want = oracle.e4m3_encode_array(448.0 * 2.0 ** -np.arange(G))
+    want[1::2] |= 0x80
+    assert np.array_equal(codes.ravel(), want)
+    assert codes[0, 0] == 0x7E
+
+
+@pytest.mark.parametrize("G", [16, 128])
+def test_round_trip_error_bound_and_degenerate_groups(G):
+    rows, cols = 20, 2 * G
+    x = _act(rows, cols, 7 * G).float()
+    x[3, :G] = 0.0                      # all-zero group
+    x[4, G:] = 0.0
+    x[4, G + 5] = -1.5                  # single nonzero
+    xb = x.to(torch.bfloat16)
+    codes, scales, _ = oracle.quantize_act(_bits(xb), rows, cols, G)
+    assert scales[3, 0] == 0 and not codes[3, :G].any()
+    assert codes[4, G + 5] == 0xFE and np.count_nonzero(codes[4, G:]) == 1
+    back = oracle.e4m3_decode_array(codes.ravel()).reshape(rows, cols) * \
+        np.repeat(scales.astype(np.float64), G, axis=1)
+    xf = xb.float().numpy().astype(np.float64)
+    normal = (codes & 0x7F) >= 0x08
+    rel = np.abs(back[normal] - xf[normal]) / np.abs(xf[normal])
+    assert rel.max() <= 2.0 ** -4 * (1 + 1e-6)
+    assert np.array_equal(np.signbit(back[normal]), np.signbit(xf[normal]))
+    sub = ((codes & 0x7F) < 0x08) & (xf != 0)
+    scale_full = np.repeat(scales.astype(np.float64), G, axis=1)
+    assert np.all(np.abs(back[sub] - xf[sub]) <= 2.0 ** -10 * scale_full[sub] * (1 + 1e-6))
+
+
+def test_memory_overhead_row_of_group_size_table():
+    rec = json.load(open(GOLDEN))
+    for G, pct in zip(rec["group_size"], rec["memory_overhead_percent"]):
+        rows, cols = 8, 4 * G
+        x = _act(rows, cols, G)
+        _, scales, _ = oracle.quantize_act(_bits(x), rows, cols, G)
+        overhead = 100.0 * scales.nbytes / (x.numel() * 2)          # vs BF16 data
+        assert overhead == pytest.approx(pct, rel=0.05)
+
+
+def test_per_group_beats_per_tensor_on_outliers():
+    rows, cols = 64, 512
+    x = _act(rows, cols, 3)
+    bits = _bits(x)
+    xf = x.float().numpy().astype(np.float64)
+
+    def mse(codes, scales, G):
+        back = oracle.e4m3_decode_array(codes.ravel()).reshape(codes.shape) * \
+            np.repeat(scales.astype(np.float64), G, axis=1)
+        return np.mean((back.reshape(rows, cols) - xf) ** 2)
+
+    c16, s16, _ = oracle.quantize_act(bits, rows, cols, 16, transpose=False)
+    ct, st, _ = oracle.quantize_act(bits, 1, rows * cols, rows * cols, transpose=False)
+    per_tensor = mse(ct.reshape(rows, cols), np.full((rows, 1), st[0, 0], np.float32), cols)
+    assert mse(c16, s16, 16) < per_tensor
+
+
+def test_rejects_ragged_group():
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize_act(np.zeros(30, np.uint16), 1, 30, 16)

@@ -30,7 +30,7 @@ COAT_ERR_HIP = 5
 
 EXPORTED_SYMBOLS = (
     "coat_adamw_fp8_step", "coat_fp8_expand_quantize", "coat_fp8_dequantize_expand",
-    "coat_e4m3_encode", "coat_e4m3_decode", "coat_status_string",
+    "coat_e4m3_encode", "coat_e4m3_decode", "coat_fp8_quantize_act", "coat_status_string",
     "coat_last_hip_error", "coat_abi_version",
 )
 
@@ -75,6 +75,8 @@ def _load(path: str = LIB_PATH):
     lib.coat_e4m3_encode.argtypes = [vp, i64, vp, vp]
     lib.coat_e4m3_decode.restype = ctypes.c_int
     lib.coat_e4m3_decode.argtypes = [vp, i64, vp, vp]
+    lib.coat_fp8_quantize_act.restype = ctypes.c_int
+    lib.coat_fp8_quantize_act.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
     lib.coat_status_string.restype = ctypes.c_char_p
     lib.coat_status_string.argtypes = [ctypes.c_int]
     lib.coat_last_hip_error.restype = ctypes.c_char_p
@@ -198,3 +200,16 @@ def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None):
 
 def e4m3_decode(codes: torch.Tensor, x: torch.Tensor, stream=None):
     _check(lib.coat_e4m3_decode(_ptr(codes), codes.numel(), _ptr(x), _stream(stream)))
+
+
+def quantize_act(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                 codes_t: Optional[torch.Tensor] = None, group_size: int = 128,
+                 stream=None):
+    """Per-group (1 x group_size) E4M3 quantization of a 2-D BF16 matrix x into
+    codes (same shape, uint8), scales (rows x cols/group_size, float32) and,
+    if given, codes_t (cols x rows, uint8)."""
+    if x.dim() != 2:
+        raise ValueError("quantize_act expects a 2-D (rows, cols) tensor")
+    rows, cols = x.shape
+    _check(lib.coat_fp8_quantize_act(_ptr(x), rows, cols, group_size, _ptr(codes),
+                                     _ptr(scales), _ptr(codes_t), _stream(stream)))

@@ -195,3 +195,71 @@ def fill_gradients(shard, step: int, stds: Sequence[float], kind: str = "gaussia
         e = shard.element_range(i)
         shard.grad[e].copy_(gradient(shard.numels[i], stds[i], step, i, shard.grad.device,
                                      kind=kind, group_size=shard.group_size))
+
+
+# ------------------------------------------------ activation matrices
+# Inputs of the per-group activation quantizer: a row-major (tokens, channels)
+# BF16 matrix, the output of a non-linear layer.
+
+ACT_OUTLIER_FRACTION = 0.01          # channels with a large, fixed gain
+ACT_OUTLIER_GAIN = (10.0, 100.0)     # log-uniform gain of those channels
+ACT_TIE_MIDPOINTS = (17.0, 8.5, 19.0, 9.5, 248.0, 3.0 * 2.0 ** -10)
+
+
+def activation(rows: int, cols: int, seed: int, device, kind: str = "llm",
+               group_size: int = DEFAULT_GROUP_SIZE) -> torch.Tensor:
+    """Seeded synthetic activation matrix, BF16 of shape (rows, cols).
+
+    ``llm``: N(0, 1) per element times a per-channel gain that is 1 except on
+    ACT_OUTLIER_FRACTION of the channels (log-uniform gain in ACT_OUTLIER_GAIN),
+    the outlier-channel structure of transformer activations.
+
+    ``stress`` adds, per 1 x group_size group of a row (a uniform draw picks
+    the class): 2% all-zero; 2% a single nonzero; 2% magnitudes scaled by
+    1e-39 (BF16 subnormals); 2% by 2^-110 (normal, below 2^-100); 2% by 1e30;
+    4% tie groups (one element +-448 * 2^e, the rest +-midpoints between
+    neighbouring E4M3 values times 2^e, e in {-20, -7, 0, 10}); 2% with -0.0 on
+    every other element; 2% wide groups (one element +-1e30, the rest N(0,1)
+    times 1e-20 in half of them, whose scaled values underflow FP32, and times
+    1e-5 in the other half, which scale to tiny normal FP32 values)."""
+    if cols % group_size:
+        raise ValueError("cols must be a multiple of group_size")
+    gen = generator(device, _seed(seed, 31, rows, cols))
+    x = torch.randn(rows, cols, generator=gen, device=device, dtype=torch.float32)
+    cgen = generator(device, _seed(seed, 32, cols))
+    outlier = torch.rand(cols, generator=cgen, device=device) < ACT_OUTLIER_FRACTION
+    lo, hi = math.log(ACT_OUTLIER_GAIN[0]), math.log(ACT_OUTLIER_GAIN[1])
+    gain = torch.exp(lo + (hi - lo) * torch.rand(cols, generator=cgen, device=device))
+    x = x * torch.where(outlier, gain, torch.ones_like(gain))
+    if kind == "llm":
+        return x.to(torch.bfloat16)
+    if kind != "stress":
+        raise KeyError(kind)
+    ng = cols // group_size
+    sgen = generator(device, _seed(seed, 33, rows, cols, group_size))
+    u = torch.rand(rows, ng, generator=sgen, device=device)
+    u = u.repeat_interleave(group_size, dim=1)           # class of each element's group
+    within = torch.arange(cols, device=device).remainder(group_size).expand(rows, cols)
+    pick = torch.randint(0, group_size, (rows, ng), generator=sgen, device=device)
+    lead = within == pick.repeat_interleave(group_size, dim=1)
+    sign = torch.where(torch.rand(rows, cols, generator=sgen, device=device) < 0.5, -1.0, 1.0)
+    e = torch.tensor([-20.0, -7.0, 0.0, 10.0], device=device)
+    escale = torch.exp2(e[torch.randint(0, 4, (rows, ng), generator=sgen, device=device)])
+    escale = escale.repeat_interleave(group_size, dim=1)
+    mids = torch.tensor(ACT_TIE_MIDPOINTS, device=device)
+    mid = mids[torch.randint(0, len(ACT_TIE_MIDPOINTS), (rows, cols), generator=sgen,
+                             device=device)]
+    zero = torch.zeros_like(x)
+    x = torch.where(u < 0.02, zero, x)
+    x = torch.where((u >= 0.02) & (u < 0.04) & ~lead, zero, x)
+    x = torch.where((u >= 0.04) & (u < 0.06), x * 1e-39, x)
+    x = torch.where((u >= 0.06) & (u < 0.08), x * 2.0 ** -110, x)
+    x = torch.where((u >= 0.08) & (u < 0.10), x * 1e30, x)
+    tie = (u >= 0.10) & (u < 0.14)
+    x = torch.where(tie, sign * escale * torch.where(lead, 448.0, mid), x)
+    negz = (u >= 0.14) & (u < 0.16) & (within % 2 == 1)
+    x = torch.where(negz, torch.full_like(x, -0.0), x)
+    wide = (u >= 0.16) & (u < 0.18)
+    rest = torch.where(u < 0.17, 1e-20, 1e-5)
+    x = torch.where(wide, torch.where(lead, sign * 1e30, x * rest), x)
+    return x.to(torch.bfloat16)

@@ -17,6 +17,12 @@ Prints ONE JSON line: Gparam/s over the timed steps, plus the step kernel's
 roofline position (algorithmic bytes per launch / average launch duration,
 HIP events on the launch stream) and the CPU oracle timed on a bounded sample
 on the host cores.
+
+``--path act_quant`` measures the per-group activation quantizer instead: one
+step quantizes a (tokens x channels) BF16 matrix (default 8192 x 11008: four
+2048-token sequences at the Llama-2-7B FFN width) into E4M3 codes, per-group
+scales and the transposed codes; it reports Gelem/s and the same roofline and
+CPU-oracle objects.
 """
 from __future__ import annotations
 
@@ -33,14 +39,22 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_adamw_fp8_step_llama2_7b.txt")
+PMC_SUMMARY_ACT = os.path.join(ROOT, "profiles", "pmc_quantize_act_8192x11008.txt")
 KERNEL_SRC = os.path.join(ROOT, "adamw_coat_fp8_amd", "csrc", "coat_fp8.hip")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--path", choices=("adamw_step", "act_quant"), default="adamw_step")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 200 for act_quant)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default 5; 20 for act_quant)")
+    ap.add_argument("--act-shape", default="8192x11008",
+                    help="rows x cols of the activation matrix (act_quant)")
+    ap.add_argument("--no-transpose", action="store_true",
+                    help="act_quant without the transposed copy")
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--group-size", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -48,7 +62,13 @@ def parse():
                     help="parameters in the oracle's timing sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (PMC calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    act = args.path == "act_quant"
+    if args.steps is None:
+        args.steps = 200 if act else 20
+    if args.warmup is None:
+        args.warmup = 20 if act else 5
+    return args
 
 
 def algorithmic_bytes(n: int, G: int) -> int:
@@ -61,13 +81,19 @@ def kernel_source_sha():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_profile(nbytes_per_launch):
+def act_bytes(rows: int, cols: int, G: int, transpose: bool = True) -> int:
+    """Read x (2 B per element); write codes (1 B), the transposed codes (1 B)
+    and one FP32 scale per group."""
+    return rows * cols * (3 + (1 if transpose else 0)) + 4 * rows * (cols // G)
+
+
+def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY):
     """HBM traffic per launch from the committed rocprofv3 PMC summary, if it
     was taken on the current kernel source; else None."""
-    if not os.path.exists(PMC_SUMMARY):
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
@@ -122,6 +148,113 @@ def cpu_baseline(specs, G, hp, sample_params):
                       f"tensors, one warm step (after one untimed step), {dt:.2f} s wall"}
 
 
+def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):
+    """The oracle's activation quantizer timed on the same matrix, split over
+    host threads by row blocks (rows are independent), repeated over whole
+    passes until at least `min_seconds` of wall time."""
+    import numpy as np
+    import oracle
+    from adamw_coat_fp8_amd import inputs
+
+    x = inputs.activation(rows, cols, 0, "cpu", "llm", G)
+    bits = inputs.bf16_bits(x).numpy().view(np.uint16)
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    blocks = np.array_split(np.arange(rows), threads)
+
+    def run(rs):
+        if len(rs):
+            oracle.quantize_act(bits[rs[0]:rs[-1] + 1], len(rs), cols, G, transpose=transpose)
+
+    passes = 0
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(run, blocks))                      # untimed pass
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(run, blocks))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"value": passes * rows * cols / dt / 1e9, "unit": "Gelem/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {rows}x{cols} matrix, {passes} passes after an untimed one, "
+                      f"{dt:.2f} s wall"}
+
+
+def bench_act(args):
+    import torch
+    from adamw_coat_fp8_amd import coat, inputs
+
+    G = args.group_size
+    rows, cols = (int(v) for v in args.act_shape.lower().split("x"))
+    transpose = not args.no_transpose
+    print(f"[bench] act_quant {rows}x{cols} G={G} transpose={transpose}",
+          file=sys.stderr, flush=True)
+    torch.cuda.init()
+    x = inputs.activation(rows, cols, 0, "cuda", "llm", G)
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((rows, cols // G), dtype=torch.float32, device="cuda")
+    codes_t = torch.empty((cols, rows), dtype=torch.uint8, device="cuda") if transpose else None
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        coat.quantize_act(x, codes, scales, codes_t, group_size=G, stream=stream)
+    torch.cuda.synchronize()
+    print(f"[bench] {args.warmup} warm-up calls done", file=sys.stderr, flush=True)
+    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        events[k][0].record(stream)
+        coat.quantize_act(x, codes, scales, codes_t, group_size=G, stream=stream)
+        events[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    avg_launch_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    nbytes = act_bytes(rows, cols, G, transpose)
+    achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    print(f"[bench] {args.steps} timed calls: {ms_per_step * 1e3:.1f} us/call wall, "
+          f"avg launch {avg_launch_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    traffic = traffic_from_profile(nbytes, PMC_SUMMARY_ACT) if transpose else None
+    rec = {
+        "metric": "Gelem/s per per-group E4M3 activation quantization (codes + transposed "
+                  "codes) + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(rows * cols / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"activation {rows}x{cols} BF16 (tokens x channels), 1x{G} groups, "
+                        f"E4M3 codes{' + transposed codes' if transpose else ''} + FP32 scales",
+            "group_size": G,
+            "algorithmic_bytes_per_step": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": f"quantize_act_kernel<{G}, {'true' if transpose else 'false'}>",
+            "bytes_per_launch": nbytes,
+            "avg_launch_ms": round(avg_launch_ms, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_act(rows, cols, G, transpose)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -129,6 +262,8 @@ def main():
               "the step is shard-local and would run unchanged on each GPU's shard.",
               file=sys.stderr)
         sys.exit(2)
+    if args.path == "act_quant":
+        return bench_act(args)
     import torch
     from adamw_coat_fp8_amd import coat, inputs
     from adamw_coat_fp8_amd.shard import FP8AdamWShard

@@ -144,6 +144,34 @@ coat_status_t coat_e4m3_encode(const float* x, int64_t n, uint8_t* codes,
 coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x,
                                hipStream_t stream);
 
+/*
+ * Per-group FP8 quantization of an activation matrix, with its transpose
+ * ([P1] section 三, 混合粒度激活量化: non-linear layers quantize per 1xG
+ * group; Triton优化内核 / 非线性层优化: that kernel also writes the transposed
+ * FP8 tensor the backward pass reads; [P1] 核心公式 FP8量化 with
+ * S = max|X| / 448).  No range expansion (k = 1).
+ *   x        rows x cols BF16 values (bit patterns), row-major (read only).
+ *   codes    rows x cols E4M3 codes, row-major (written).
+ *   scales   rows x (cols / group_size) FP32, row-major (written): group
+ *            (i, j) covers x[i, j*G .. j*G+G-1] and stores S = max|x| / 448
+ *            (IEEE division; 0 for an all-zero group).
+ *   codes_t  cols x rows E4M3 codes, the transpose of `codes` (written), or
+ *            NULL to skip it.
+ * Each code is RNE_E4M3(x * r) with r = 448 / max|x| rounded to FP32 and the
+ * product rounded to FP32 (groups with max < 2^-100 compute both as if FP32
+ * had an unbounded exponent); -0 gives code 0x00, an all-zero group codes 0.
+ * cols must be a multiple of group_size.  x, codes and codes_t 16-byte
+ * aligned, scales 4-byte aligned; writes into codes_t are 16 bytes wide when
+ * rows is a multiple of 16, bytes otherwise.
+ * Errors: NULL_POINTER (x/codes/scales NULL with rows, cols > 0),
+ * INVALID_VALUE (rows or cols < 0, cols % group_size != 0, more than 2^31-1
+ * tiles of 64 x 128), GROUP_SIZE, MISALIGNED, HIP.
+ */
+coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows,
+                                    int64_t cols, int32_t group_size,
+                                    uint8_t* codes, float* scales,
+                                    uint8_t* codes_t, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* coat_status_string(coat_status_t status);
 

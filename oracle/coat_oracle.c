@@ -327,10 +327,16 @@ int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
         for (int64_t j = c0; j < c0 + group_size; ++j) codes[i * cols + j] = 0x00;
         continue;
       }
-      const float r = (float)kE4M3Max / amax;
+      /* r = 448 / max and q = x * r, each rounded to FP32.  Below 2^-100 the
+       * quotient would overflow FP32's exponent range, so such groups scale
+       * max and x by 2^64 first (exact; the rounded results are those of an
+       * FP32 with unbounded exponent). */
+      const int tiny = amax < 0x1p-100f;
+      const float pre = tiny ? 0x1p64f : 1.0f;
+      const float r = (float)kE4M3Max / (amax * pre);
       scales[i * groups_per_row + gj] = amax / (float)kE4M3Max;
       for (int64_t j = c0; j < c0 + group_size; ++j) {
-        const float q = bf16_to_float(x_bf16[i * cols + j]) * r;
+        const float q = (bf16_to_float(x_bf16[i * cols + j]) * pre) * r;
         codes[i * cols + j] = coat_oracle_e4m3_encode((double)q);
       }
     }

@@ -97,7 +97,8 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
  * [P1] eq. FP8量化 with S = max|X| / 448 per group).  Reading: the rounding
  * decision is taken in FP32, r = 448 / max (IEEE division), code =
  * RNE(x * r); the stored scale is S = max / 448 (IEEE division); an all-zero
- * group stores S = 0 and codes 0.  cols must be a multiple of group_size.
+ * group stores S = 0 and codes 0.  Groups with max < 2^-100 take r and x*r
+ * as an FP32 with unbounded exponent range would (exact 2^64 prescale).  cols must be a multiple of group_size.
  * codes: rows x cols, scales: rows x cols/group_size, codes_t: cols x rows
  * (the transpose of codes; may be NULL). */
 int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,

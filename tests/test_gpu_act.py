@@ -1,0 +1,165 @@
+"""GPU parity of the per-group activation quantizer (coat_fp8_quantize_act)
+against the oracle: bit-exact codes, scales and transposed codes.  Both sides
+take every rounding decision in FP32 (r = 448 / max, x * r, max / 448), so no
+tolerance applies.  Cases: every group size over tile-aligned and ragged
+shapes (rows not a multiple of 64 or 16, cols not a multiple of 128), the
+stress recipe (zero, single-nonzero, subnormal, tiny, huge, tie, -0.0 and
+wide-range groups), the variant without the transpose, the full 8192 x 11008
+shape on sampled rows plus the transpose property over every element, and
+host-side rejection of bad arguments."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adamw_coat_fp8_amd import inputs
+from gpu_util import DEV, bits_np, lib, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xA5          # output bytes the kernel must overwrite
+
+
+def setup_module():
+    require_gpu()
+
+
+def _outputs(rows, cols, G, transpose=True):
+    codes = torch.full((rows, cols), SENTINEL, dtype=torch.uint8, device=DEV)
+    scales = torch.full((rows, cols // G), float("nan"), dtype=torch.float32, device=DEV)
+    codes_t = (torch.full((cols, rows), SENTINEL, dtype=torch.uint8, device=DEV)
+               if transpose else None)
+    return codes, scales, codes_t
+
+
+def _gpu(x, G, transpose=True):
+    coat = lib()
+    rows, cols = x.shape
+    codes, scales, codes_t = _outputs(rows, cols, G, transpose)
+    coat.quantize_act(x, codes, scales, codes_t, group_size=G)
+    torch.cuda.synchronize()
+    return (codes.cpu().numpy(), scales.cpu().numpy(),
+            None if codes_t is None else codes_t.cpu().numpy())
+
+
+def _oracle(x, G):
+    rows, cols = x.shape
+    return oracle.quantize_act(bits_np(x).reshape(rows, cols), rows, cols, G, transpose=True)
+
+
+def _assert_same(tag, gpu, ref):
+    gc, gs, gt = gpu
+    rc, rs, rt = ref
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{tag}: {len(bad)} codes differ, first at {bad[:4].tolist()}: " \
+                          f"gpu {gc[tuple(bad[0])]:#04x} oracle {rc[tuple(bad[0])]:#04x}"
+    sbad = np.argwhere(gs.view(np.uint32) != rs.view(np.uint32))
+    assert sbad.size == 0, f"{tag}: {len(sbad)} scales differ, first at {sbad[:4].tolist()}"
+    if gt is not None:
+        tbad = np.argwhere(gt != rt)
+        assert tbad.size == 0, f"{tag}: {len(tbad)} transposed codes differ, first at " \
+                               f"{tbad[:4].tolist()}"
+
+
+SHAPES = [(1, 128), (3, 256), (64, 128), (65, 384), (130, 1024), (256, 640), (48, 4096),
+          (17, 1152)]
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{r}x{c}" for r, c in SHAPES])
+def test_llm_shapes_bit_exact(G, shape):
+    rows, cols = shape
+    x = inputs.activation(rows, cols, 1, DEV, "llm", G)
+    print(f"[act] llm {rows}x{cols} G={G}", flush=True)
+    _assert_same(f"llm {rows}x{cols} G={G}", _gpu(x, G), _oracle(x, G))
+
+
+@pytest.mark.parametrize("shape,G", [((37, 48), 16), ((70, 96), 32), ((129, 192), 64),
+                                     ((5, 16), 16), ((200, 32), 32)])
+def test_partial_column_tiles(shape, G):
+    rows, cols = shape
+    x = inputs.activation(rows, cols, 2, DEV, "llm", G)
+    print(f"[act] partial {rows}x{cols} G={G}", flush=True)
+    _assert_same(f"partial {rows}x{cols} G={G}", _gpu(x, G), _oracle(x, G))
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+@pytest.mark.parametrize("shape", [(200, 1024), (77, 640), (64, 2048)])
+def test_stress_bit_exact(G, shape):
+    rows, cols = shape
+    x = inputs.activation(rows, cols, 3, DEV, "stress", G)
+    print(f"[act] stress {rows}x{cols} G={G}", flush=True)
+    ref = _oracle(x, G)
+    # the recipe reaches the cases it is meant to: zero groups, signed zero codes
+    assert (ref[1] == 0).any() and (ref[0] == 0x80).any()
+    _assert_same(f"stress {rows}x{cols} G={G}", _gpu(x, G), ref)
+
+
+@pytest.mark.parametrize("G", [16, 128])
+def test_without_transpose_same_codes(G):
+    x = inputs.activation(96, 512, 4, DEV, "stress", G)
+    a = _gpu(x, G, transpose=True)
+    b = _gpu(x, G, transpose=False)
+    assert b[2] is None
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32),
+                                                          b[1].view(np.uint32))
+
+
+def test_full_size_sampled_rows():
+    """8192 x 11008 (4 sequences of 2048 tokens, FFN width 11008), G = 128, in
+    the launch the benchmark times.  Oracle on 48 sampled rows (each row is
+    independent), and codes_t == codes^T checked over every element on the
+    device."""
+    coat = lib()
+    rows, cols, G = 8192, 11008, 128
+    x = inputs.activation(rows, cols, 0, DEV, "llm", G)
+    codes, scales, codes_t = _outputs(rows, cols, G)
+    coat.quantize_act(x, codes, scales, codes_t, group_size=G)
+    torch.cuda.synchronize()
+    assert torch.equal(codes_t, codes.t().contiguous())
+    sel = np.sort(np.random.default_rng(0).choice(rows, 48, replace=False))
+    sel[0], sel[-1] = 0, rows - 1
+    sub = x[torch.from_numpy(sel).to(DEV)]
+    rc, rs, _ = _oracle(sub, G)
+    gc = codes.cpu().numpy()[sel]
+    gs = scales.cpu().numpy()[sel]
+    assert np.array_equal(gc, rc)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+def test_empty_is_noop_and_bad_arguments_rejected():
+    coat = lib()
+    vp = ctypes.c_void_p
+    x = inputs.activation(32, 256, 5, DEV, "llm", 128)
+    codes, scales, codes_t = _outputs(32, 256, 16)
+    snap = [t.clone() for t in (codes, scales, codes_t)]
+    raw = coat.lib.coat_fp8_quantize_act
+    s = torch.cuda.current_stream().cuda_stream
+    xp, cp, sp, tp = x.data_ptr(), codes.data_ptr(), scales.data_ptr(), codes_t.data_ptr()
+    cases = [
+        ((xp, 0, 256, 16, cp, sp, tp), coat.COAT_OK),            # empty: nothing written
+        ((xp, 32, 0, 16, cp, sp, tp), coat.COAT_OK),
+        ((None, 0, 0, 16, None, None, None), coat.COAT_OK),
+        ((xp, -1, 256, 16, cp, sp, tp), coat.COAT_ERR_INVALID_VALUE),
+        ((xp, 32, 250, 16, cp, sp, tp), coat.COAT_ERR_INVALID_VALUE),   # cols % G
+        ((xp, 32, 256, 24, cp, sp, tp), coat.COAT_ERR_GROUP_SIZE),
+        ((None, 32, 256, 16, cp, sp, tp), coat.COAT_ERR_NULL_POINTER),
+        ((xp, 32, 256, 16, None, sp, tp), coat.COAT_ERR_NULL_POINTER),
+        ((xp, 32, 256, 16, cp, None, tp), coat.COAT_ERR_NULL_POINTER),
+        ((xp + 2, 32, 128, 16, cp, sp, tp), coat.COAT_ERR_MISALIGNED),
+        ((xp, 32, 256, 16, cp + 8, sp, tp), coat.COAT_ERR_MISALIGNED),
+        ((xp, 32, 256, 16, cp, sp + 2, tp), coat.COAT_ERR_MISALIGNED),
+        ((xp, 32, 256, 16, cp, sp, tp + 4), coat.COAT_ERR_MISALIGNED),
+    ]
+    for args, want in cases:
+        got = raw(*[vp(a) if a is not None else None for a in args[:1]], args[1], args[2],
+                  args[3], *[vp(a) if a is not None else None for a in args[4:]], vp(s))
+        assert got == want, (args, got, want)
+    torch.cuda.synchronize()
+    # bit patterns: the scale sentinel is NaN
+    assert torch.equal(codes, snap[0]) and torch.equal(codes_t, snap[2])
+    assert torch.equal(scales.view(torch.int32), snap[1].view(torch.int32))
+    with pytest.raises(coat.CoatError):
+        coat.quantize_act(x, codes, scales, codes_t, group_size=24)

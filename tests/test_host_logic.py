@@ -96,3 +96,34 @@ def test_stress_recipe_features():
     assert (nnz == 1).any() and (nnz == 0).any()     # single-nonzero and all-zero groups
     assert np.any(np.isclose(np.abs(g), 4.5e-15, rtol=0.01))   # tiny magnitudes
     assert inputs.gradient(n, 1e-3, 1, 0, "cpu", kind="stress", group_size=G).dtype == torch.bfloat16
+
+
+def test_bench_act_byte_accounting():
+    sys.path.insert(0, ROOT)
+    import bench
+    # read BF16 2 B, write codes 1 B + transposed codes 1 B, FP32 scale per group
+    assert bench.act_bytes(8192, 11008, 128) == 8192 * 11008 * 4 + 4 * 8192 * 86 == 363_528_192
+    assert bench.act_bytes(8192, 11008, 16, transpose=False) == 8192 * 11008 * 3 + 4 * 8192 * 688
+
+
+def test_activation_recipe_features():
+    rows, cols = 256, 1024
+    x = inputs.activation(rows, cols, 0, "cpu", "llm", 128)
+    assert x.dtype == torch.bfloat16 and x.shape == (rows, cols)
+    ch = x.float().abs().amax(0)
+    assert 3 <= int((ch > 20).sum()) <= 40                      # ~1% outlier channels
+    assert torch.equal(x, inputs.activation(rows, cols, 0, "cpu", "llm", 128))
+    for G in (16, 128):
+        s = inputs.activation(rows, cols, 3, "cpu", "stress", G).float()
+        grp = s.reshape(rows, cols // G, G)
+        amax = grp.abs().amax(-1)
+        nnz = (grp != 0).sum(-1)
+        assert (amax == 0).any() and (nnz == 1).any()           # zero and single-nonzero
+        assert ((amax > 0) & (amax < 2.0 ** -126)).any()        # subnormal groups
+        assert ((amax >= 2.0 ** -126) & (amax < 2.0 ** -100)).any()
+        assert (amax > 1e29).any()
+        assert (torch.signbit(s) & (s == 0)).any()              # -0.0 entries
+        tie = (amax / 448.0).log2()
+        assert ((tie == tie.round()) & (amax > 0)).any()        # max = 448 * 2^e
+    with pytest.raises(ValueError):
+        inputs.activation(4, 100, 0, "cpu", "llm", 16)

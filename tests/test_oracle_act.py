@@ -114,3 +114,68 @@ def test_per_group_beats_per_tensor_on_outliers():
 def test_rejects_ragged_group():
     with pytest.raises(oracle.OracleError):
         oracle.quantize_act(np.zeros(30, np.uint16), 1, 30, 16)
+
+
+@pytest.mark.parametrize("G", [16, 128])
+def test_tiny_groups_are_scale_invariant(G):
+    """Groups with max |x| < 2^-100 (including BF16 subnormals, where 448/max
+    overflows FP32) quantize as FP32 with an unbounded exponent would: their
+    codes equal those of the same group times 2^64, a normal-range group; the
+    scale is still the FP32 quotient max/448."""
+    rows, cols = 12, 2 * G
+    base = _act(rows, cols, 11 * G, outliers=False).float().numpy().astype(np.float64)
+    factors = np.array([1e-39, 2.0 ** -110, 2.0 ** -101, 3e-38, 1e-32, 2.0 ** -126,
+                        1e-40, 2.0 ** -99, 5e-31, 1e-36, 2.0 ** -120, 7e-34])
+    tiny = torch.from_numpy(base * factors[:, None]).to(torch.bfloat16)
+    big = (tiny.double() * 2.0 ** 64).to(torch.bfloat16)
+    assert torch.equal(big.double(), tiny.double() * 2.0 ** 64)       # exact scaling
+    assert (tiny.float().abs().amax(1) < 2.0 ** -100).sum() >= 8
+    ct, st, _ = oracle.quantize_act(_bits(tiny), rows, cols, G)
+    cb, _, _ = oracle.quantize_act(_bits(big), rows, cols, G)
+    assert np.array_equal(ct, cb)
+    amax = tiny.float().reshape(rows, cols // G, G).abs().amax(-1).numpy()
+    assert np.array_equal(st, amax / np.float32(448.0))             # numpy FP32 division
+    # subnormal BF16 groups (max below 2^-126) still spread over the code range
+    sub = tiny.float().abs().amax(1).numpy() < 2.0 ** -126
+    assert sub.any() and (ct[sub] & 0x7F).max() == 0x7E
+
+
+def test_negative_zero_and_signed_underflow():
+    """-0.0 gives code 0x00; a negative value whose scaled magnitude is below
+    half the smallest E4M3 subnormal keeps its sign (0x80); one whose FP32
+    product underflows to -0 gives 0x00."""
+    G = 16
+    v = np.zeros(G, np.float32)
+    v[0] = 1.0
+    v[1] = -0.0
+    v[2] = -2.0 ** -20            # x * 448 = -4.3e-4 < 2^-10 -> E4M3 -0 (0x80)
+    v[3] = 2.0 ** -20
+    x = torch.from_numpy(v).reshape(1, G).to(torch.bfloat16)
+    c, _, _ = oracle.quantize_act(_bits(x), 1, G, G)
+    assert c[0, 0] == 0x7E and c[0, 1] == 0x00 and c[0, 2] == 0x80 and c[0, 3] == 0x00
+    w = np.zeros(G, np.float32)
+    w[0] = 1e30
+    w[1] = -1e-20                 # 448e-50 underflows FP32 to -0 -> 0x00
+    w[2] = -1e-5                  # tiny normal FP32 product -> 0x80
+    y = torch.from_numpy(w).reshape(1, G).to(torch.bfloat16)
+    c, _, _ = oracle.quantize_act(_bits(y), 1, G, G)
+    assert c[0, 1] == 0x00 and c[0, 2] == 0x80
+
+
+def test_ties_round_to_even():
+    """A group whose max is 448 * 2^e has r = 2^-e exactly, so midpoints
+    between neighbouring E4M3 values times 2^e are exact ties: they go to
+    the even code (17 -> 16, 19 -> 20, 8.5 -> 8, 9.5 -> 10, 248 -> 256,
+    3 * 2^-10 -> 2^-8)."""
+    G = 16
+    mids = [17.0, 19.0, 8.5, 9.5, 248.0, 3.0 * 2.0 ** -10]
+    want = [16.0, 20.0, 8.0, 10.0, 256.0, 2.0 ** -8]
+    for e in (-20, 0, 10):
+        v = np.zeros(G, np.float64)
+        v[0] = 448.0 * 2.0 ** e
+        v[1:1 + len(mids)] = np.array(mids) * 2.0 ** e
+        x = torch.from_numpy(v).reshape(1, G).to(torch.bfloat16)
+        assert torch.equal(x.double(), torch.from_numpy(v).reshape(1, G))
+        c, _, _ = oracle.quantize_act(_bits(x), 1, G, G)
+        got = oracle.e4m3_decode_array(c.ravel()[1:1 + len(mids)])
+        assert np.array_equal(got, want)

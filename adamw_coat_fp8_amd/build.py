@@ -8,7 +8,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "coat_fp8.hip")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("coat_fp8.hip", "coat_act.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcoat_fp8.so")
 ARCH = "gfx950"
@@ -29,7 +29,7 @@ def hipcc():
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", LIB + ".tmp", SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", LIB + ".tmp", *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

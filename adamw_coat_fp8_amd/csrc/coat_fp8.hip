@@ -27,15 +27,25 @@
 
 #include <algorithm>
 
-#include "coat_fp8.h"
+#include "coat_common.h"
+
+namespace coat {
+
+thread_local char g_last_hip_error[256] = "";
+
+coat_status_t hip_fail(hipError_t e) {
+  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
+  return COAT_ERR_HIP;
+}
+
+}  // namespace coat
+
+using namespace coat;
 
 namespace {
 
-constexpr int kWave = 64;
 constexpr int kElemsPerLane = 16;
 constexpr int kTileElems = kWave * kElemsPerLane;  // 1024
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kMaxTensorsPerLaunch = 40;
 
 // [OCP] E4M3: log2 of the largest finite value 448, and log2 of its dynamic
@@ -176,8 +186,6 @@ __device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHigh);
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Group reductions over the G/16 lanes that hold one group (lanes are
 // consecutive and the group starts at a multiple of G/16).  Quad steps swap
@@ -742,193 +750,8 @@ __global__ __launch_bounds__(kBlockThreads) void e4m3_decode_kernel(const uint8_
     x[i] = __builtin_amdgcn_cvt_f32_fp8((int)codes[i], 0);
 }
 
-// ------------------------------------------- per-group activation quantizer
-//
-// [P1] section 三, mixed-granularity activation quantization: the tensors of
-// non-linear layers are quantized per 1xG group of a row with the FP8量化
-// equation (S = max|X| / 448, X_FP8 = round(X / S)), and the non-linear-layer
-// kernel emits the FP8 tensor together with its transpose for the backward
-// pass.  No expansion here (k = 1).
-//
-// One block of 256 threads takes a tile of kActTileRows rows x 128 columns.
-// Load phase: 16 threads cover one 128-column row (16 B = 8 BF16 each), so a
-// wave reads 4 rows and a group of G columns sits on G/8 consecutive lanes of
-// one 16-lane DPP row.  Each lane reduces its 8 magnitudes, DPP joins the
-// group, and the lane converts its values and writes 8 code bytes both to the
-// row-major output and to an LDS copy of the tile.  Transpose phase: a thread
-// reads a 16-row x 4-column block of the LDS tile as 16 dwords, transposes it
-// in registers with byte permutes and writes four 16-byte column runs, so 8
-// consecutive lanes fill 128 contiguous bytes of one row of the transpose.
-
-constexpr int kActTileCols = 128;
-constexpr int kActTileRows = 64;
-constexpr int kActPasses = kActTileRows / 16;
-constexpr int kActRowBlocks = kActTileRows / 16;
-
-struct ActParams {
-  const uint16_t* x;
-  uint8_t* codes;
-  float* scales;
-  uint8_t* codes_t;
-  int64_t rows;
-  int64_t cols;
-  int64_t col_tiles;
-  int64_t groups_per_row;
-  int32_t vec_t;  // rows % 16 == 0: 16-byte stores into the transpose
-};
-
-// Max over the kLanes lanes of a group inside one 16-lane row: quad swaps of
-// 1 and 2 lanes, then the half-row mirror (joins two quads) and the row
-// mirror (joins two halves).
-template <int kLanes>
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-  if constexpr (kLanes >= 2)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  if constexpr (kLanes >= 4)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  if constexpr (kLanes >= 8)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  if constexpr (kLanes >= 16)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  return v;
-}
-
-// Largest BF16 magnitude (as its 15 bits) among the 8 values of a chunk:
-// sign-cleared BF16 patterns order like the magnitudes they encode.
-__device__ __forceinline__ uint32_t bf16x8_max_mag(uint4 r) {
-  const uint32_t a = max(r.x & 0x7FFFu, (r.x >> 16) & 0x7FFFu);
-  const uint32_t b = max(r.y & 0x7FFFu, (r.y >> 16) & 0x7FFFu);
-  const uint32_t c = max(r.z & 0x7FFFu, (r.z >> 16) & 0x7FFFu);
-  const uint32_t d = max(r.w & 0x7FFFu, (r.w >> 16) & 0x7FFFu);
-  return max(max(a, b), max(c, d));
-}
-
-// x * r in FP32 (x already multiplied by the exact power-of-two prescale),
-// with -0 folded to +0 so that only values that round to zero in E4M3 keep a
-// negative sign.  Contraction is off: the product is rounded once, on its own.
-__device__ __forceinline__ float act_scaled(float x, float r) {
-#pragma clang fp contract(off)
-  return x * r + 0.0f;
-}
-
-__device__ __forceinline__ uint32_t act_pack4(uint32_t w0, uint32_t w1, float pre, float r) {
-  const float q0 = act_scaled(bf16_lo(w0) * pre, r), q1 = act_scaled(bf16_hi(w0) * pre, r);
-  const float q2 = act_scaled(bf16_lo(w1) * pre, r), q3 = act_scaled(bf16_hi(w1) * pre, r);
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-  v = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, v, true);
-  return (uint32_t)v;
-}
-
-// LDS tile: kActTileRows rows of 32 dwords.  The dword column is XOR-swizzled
-// by the row's 16-row block so that the transpose phase's column reads (one
-// dword from each of 16 consecutive rows, 32 lanes on distinct columns and
-// blocks) fall on distinct banks.
-__device__ __forceinline__ int act_swz(int row_block) {
-  return (row_block * (512 / kActTileRows)) & 31;
-}
-
-template <int G, bool kTranspose>
-__global__ __launch_bounds__(kBlockThreads) void quantize_act_kernel(const ActParams p) {
-  constexpr int kLanes = G / 8;
-  __shared__ uint32_t tile[kTranspose ? kActTileRows * 32 : 1];
-  const int t = threadIdx.x;
-  const int64_t tr = (int64_t)blockIdx.x / p.col_tiles;
-  const int64_t tc = (int64_t)blockIdx.x - tr * p.col_tiles;
-  const int64_t r0 = tr * kActTileRows, c0 = tc * kActTileCols;
-  const int chunk = t & 15, rsub = t >> 4;
-  const int64_t col = c0 + 8 * chunk;
-  const bool col_ok = col < p.cols;
-
-  uint4 raw[kActPasses];
-#pragma unroll
-  for (int q = 0; q < kActPasses; ++q) {
-    const int64_t row = r0 + 16 * q + rsub;
-    raw[q] = make_uint4(0, 0, 0, 0);
-    if (col_ok && row < p.rows)
-      raw[q] = *reinterpret_cast<const uint4*>(p.x + row * p.cols + col);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-  for (int q = 0; q < kActPasses; ++q) {
-    const int64_t row = r0 + 16 * q + rsub;
-    const bool ok = col_ok && row < p.rows;
-    // groups never straddle a validity boundary: a 16-lane row is one tile
-    // row, and cols is a multiple of G
-    const uint32_t mag = row16_max_u32<kLanes>(bf16x8_max_mag(raw[q]));
-    const float amax = __uint_as_float(mag << 16);
-    // Below 2^-100, 448 / max would leave FP32's range: scale max and x by 2^64
-    // (exact) so the rounded r and x*r are those of an unbounded exponent.
-    const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
-    const float r = 448.0f / (amax * pre);
-    const bool nonzero = amax > 0.0f;
-    uint2 c;
-    c.x = nonzero ? act_pack4(raw[q].x, raw[q].y, pre, r) : 0u;
-    c.y = nonzero ? act_pack4(raw[q].z, raw[q].w, pre, r) : 0u;
-    if (ok) {
-      *reinterpret_cast<uint2*>(p.codes + row * p.cols + col) = c;
-      if (chunk % kLanes == 0) p.scales[row * p.groups_per_row + col / G] = amax / 448.0f;
-    }
-    if constexpr (kTranspose) {
-      const int lr = 16 * q + rsub;
-      *reinterpret_cast<uint2*>(&tile[lr * 32 + ((2 * chunk) ^ act_swz(q))]) = c;
-    }
-  }
-
-  if constexpr (kTranspose) {
-    __syncthreads();
-    constexpr int kTasks = kActRowBlocks * 32;
-    for (int task = t; task < kTasks; task += kBlockThreads) {
-      const int rb = task % kActRowBlocks, cb = task / kActRowBlocks;
-      const int dcol = cb ^ act_swz(rb);
-      uint32_t d[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) d[i] = tile[(16 * rb + i) * 32 + dcol];
-      // out[j][b]: column 4*cb + j, rows 16*rb + 4*b .. +3 (byte 0 = first row)
-      uint32_t out[4][4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t a0 = d[4 * b], a1 = d[4 * b + 1], a2 = d[4 * b + 2], a3 = d[4 * b + 3];
-        // v_perm_b32 picks bytes of {S0:S1}, selectors 0-3 from S1, 4-7 from S0
-        const uint32_t x0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.0 a1.0 a0.1 a1.1
-        const uint32_t x1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.2 a1.2 a0.3 a1.3
-        const uint32_t y0 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
-        const uint32_t y1 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
-        out[0][b] = __builtin_amdgcn_perm(y0, x0, 0x05040100u);
-        out[1][b] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
-        out[2][b] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
-        out[3][b] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
-      }
-      const int64_t row = r0 + 16 * rb;
-      if (row >= p.rows) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t c = c0 + 4 * cb + j;
-        if (c >= p.cols) continue;
-        uint8_t* dst = p.codes_t + c * p.rows + row;
-        if (p.vec_t && row + 16 <= p.rows) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(out[j][0], out[j][1], out[j][2], out[j][3]);
-        } else {
-          for (int i = 0; i < 16 && row + i < p.rows; ++i)
-            dst[i] = (uint8_t)(out[j][i >> 2] >> (8 * (i & 3)));
-        }
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------ host side
 
-thread_local char g_last_hip_error[256] = "";
-
-coat_status_t hip_fail(hipError_t e) {
-  snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
-  return COAT_ERR_HIP;
-}
-
-bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
-
-bool valid_group_size(int32_t g) { return g == 16 || g == 32 || g == 64 || g == 128; }
 
 // One wave per tile: the grid covers every tile once (the grid-stride loops
 // in the kernels then run one iteration).  Measured on MI355X, this streams
@@ -1014,21 +837,6 @@ hipError_t launch_codec(const CodecParams& p, int32_t group_size, hipStream_t st
   if (p.n % kTileElems)
     return launch_tiles(codec_kernel_for<kQuantize>(group_size, true), 1, &q, stream);
   return hipSuccess;
-}
-
-template <int G>
-const void* act_fn(bool transpose) {
-  return transpose ? reinterpret_cast<const void*>(&quantize_act_kernel<G, true>)
-                   : reinterpret_cast<const void*>(&quantize_act_kernel<G, false>);
-}
-
-const void* act_kernel_for(int32_t g, bool transpose) {
-  switch (g) {
-    case 16: return act_fn<16>(transpose);
-    case 32: return act_fn<32>(transpose);
-    case 64: return act_fn<64>(transpose);
-    default: return act_fn<128>(transpose);
-  }
 }
 
 }  // namespace
@@ -1168,38 +976,6 @@ coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x, hipStr
   return e == hipSuccess ? COAT_OK : hip_fail(e);
 }
 
-coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows, int64_t cols,
-                                    int32_t group_size, uint8_t* codes, float* scales,
-                                    uint8_t* codes_t, hipStream_t stream) {
-  if (rows < 0 || cols < 0) return COAT_ERR_INVALID_VALUE;
-  if (!valid_group_size(group_size)) return COAT_ERR_GROUP_SIZE;
-  if (cols % group_size != 0) return COAT_ERR_INVALID_VALUE;
-  if (rows == 0 || cols == 0) return COAT_OK;
-  if (!x || !codes || !scales) return COAT_ERR_NULL_POINTER;
-  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4) ||
-      (codes_t && !aligned(codes_t, 16)))
-    return COAT_ERR_MISALIGNED;
-  ActParams p;
-  memset(&p, 0, sizeof(p));
-  p.x = x;
-  p.codes = codes;
-  p.scales = scales;
-  p.codes_t = codes_t;
-  p.rows = rows;
-  p.cols = cols;
-  p.col_tiles = (cols + kActTileCols - 1) / kActTileCols;
-  p.groups_per_row = cols / group_size;
-  p.vec_t = (rows % 16) == 0;
-  const int64_t row_tiles = (rows + kActTileRows - 1) / kActTileRows;
-  if (row_tiles > 0x7FFFFFFF / p.col_tiles) return COAT_ERR_INVALID_VALUE;
-  void* args[] = {&p};
-  const hipError_t e =
-      hipLaunchKernel(act_kernel_for(group_size, codes_t != nullptr),
-                      dim3((unsigned)(row_tiles * p.col_tiles)), dim3(kBlockThreads), args, 0,
-                      stream);
-  return e == hipSuccess ? COAT_OK : hip_fail(e);
-}
-
 const char* coat_status_string(coat_status_t status) {
   switch (status) {
     case COAT_OK: return "COAT_OK";
@@ -1212,7 +988,7 @@ const char* coat_status_string(coat_status_t status) {
   return "unknown coat_status_t";
 }
 
-const char* coat_last_hip_error(void) { return g_last_hip_error; }
+const char* coat_last_hip_error(void) { return coat::g_last_hip_error; }
 
 int32_t coat_abi_version(void) { return COAT_FP8_ABI_VERSION; }
 

@@ -40,7 +40,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_adamw_fp8_step_llama2_7b.txt")
 PMC_SUMMARY_ACT = os.path.join(ROOT, "profiles", "pmc_quantize_act_8192x11008.txt")
-KERNEL_SRC = os.path.join(ROOT, "adamw_coat_fp8_amd", "csrc", "coat_fp8.hip")
+_CSRC = os.path.join(ROOT, "adamw_coat_fp8_amd", "csrc")
+# the sources each profiled kernel is built from
+STEP_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_fp8.hip", "coat_common.h")]
+ACT_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_act.hip", "coat_common.h")]
 
 
 def parse():
@@ -77,8 +80,11 @@ def algorithmic_bytes(n: int, G: int) -> int:
     return 14 * n + 32 * ((n + G - 1) // G)
 
 
-def kernel_source_sha():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_sha(sources=STEP_SOURCES):
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def act_bytes(rows: int, cols: int, G: int, transpose: bool = True) -> int:
@@ -87,7 +93,7 @@ def act_bytes(rows: int, cols: int, G: int, transpose: bool = True) -> int:
     return rows * cols * (3 + (1 if transpose else 0)) + 4 * rows * (cols // G)
 
 
-def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY):
+def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY, sources=STEP_SOURCES):
     """HBM traffic per launch from the committed rocprofv3 PMC summary, if it
     was taken on the current kernel source; else None."""
     if not os.path.exists(path):
@@ -97,7 +103,7 @@ def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != kernel_source_sha():
+    if kv.get("kernel_source_sha") != kernel_source_sha(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -105,10 +111,12 @@ def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY):
         return None
 
 
-def cpu_baseline(specs, G, hp, sample_params):
+def cpu_baseline(specs, G, hp, sample_params, min_seconds=10.0):
     """The oracle, as it stands, timed on a bounded sample of the workload:
     the first elements of each tensor (up to 2M per tensor) until the sample is
-    full; warm state from one untimed oracle step; one timed step.  Threads
+    full; warm state from one untimed oracle step; then whole timed steps
+    (steps 2, 3, ...; the gradient of step 2 is reused, which leaves the work
+    unchanged) until at least `min_seconds` of wall time.  Threads
     split the sample by whole tensors-slices (the oracle is single-threaded
     C; ctypes releases the GIL)."""
     import numpy as np
@@ -136,16 +144,21 @@ def cpu_baseline(specs, G, hp, sample_params):
         w, g1, g2, m, v = item
         oracle.adamw_fp8_step(w, g1 if step == 1 else g2, m, v, G, **hp, step=step)
 
+    steps = 0
     with cf.ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda it: run(it, 1), work))
         t0 = time.perf_counter()
-        list(ex.map(lambda it: run(it, 2), work))
-        dt = time.perf_counter() - t0
+        while True:
+            list(ex.map(lambda it: run(it, 2 + steps), work))
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
     n_total = sum(n for _, n in pieces)
-    return {"value": n_total / dt / 1e9, "unit": "Gparam/s", "cores": threads,
+    return {"value": steps * n_total / dt / 1e9, "unit": "Gparam/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_total} params: first <=2M elements of the first {len(pieces)} "
-                      f"tensors, one warm step (after one untimed step), {dt:.2f} s wall"}
+                      f"tensors, {steps} whole steps after one untimed step, {dt:.2f} s wall"}
 
 
 def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):
@@ -181,6 +194,20 @@ def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):
                       f"{dt:.2f} s wall"}
 
 
+def copy_probe():
+    """Three 4 GiB device-to-device copies: a kernel of known traffic against
+    which the profiler's FETCH_SIZE / WRITE_SIZE counters are scaled."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("[bench] copy probe: 3 x 4 GiB device copies done", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def bench_act(args):
     import torch
     from adamw_coat_fp8_amd import coat, inputs
@@ -188,16 +215,27 @@ def bench_act(args):
     G = args.group_size
     rows, cols = (int(v) for v in args.act_shape.lower().split("x"))
     transpose = not args.no_transpose
-    print(f"[bench] act_quant {rows}x{cols} G={G} transpose={transpose}",
+    # Several independent buffer sets, used in turn, so that no call finds its
+    # input in the 256 MB last-level cache: at least 2 GiB in all.
+    nset = max(2, -(-(2 << 30) // (4 * rows * cols)))
+    print(f"[bench] act_quant {rows}x{cols} G={G} transpose={transpose}, {nset} buffer sets",
           file=sys.stderr, flush=True)
     torch.cuda.init()
-    x = inputs.activation(rows, cols, 0, "cuda", "llm", G)
-    codes = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((rows, cols // G), dtype=torch.float32, device="cuda")
-    codes_t = torch.empty((cols, rows), dtype=torch.uint8, device="cuda") if transpose else None
+    sets = []
+    for i in range(nset):
+        sets.append((inputs.activation(rows, cols, i, "cuda", "llm", G),
+                     torch.empty((rows, cols), dtype=torch.uint8, device="cuda"),
+                     torch.empty((rows, cols // G), dtype=torch.float32, device="cuda"),
+                     torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+                     if transpose else None))
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+
+    def call(k):
+        x, codes, scales, codes_t = sets[k % nset]
         coat.quantize_act(x, codes, scales, codes_t, group_size=G, stream=stream)
+
+    for k in range(args.warmup):
+        call(k)
     torch.cuda.synchronize()
     print(f"[bench] {args.warmup} warm-up calls done", file=sys.stderr, flush=True)
     events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
@@ -206,7 +244,7 @@ def bench_act(args):
     t0 = time.perf_counter()
     for k in range(args.steps):
         events[k][0].record(stream)
-        coat.quantize_act(x, codes, scales, codes_t, group_size=G, stream=stream)
+        call(k)
         events[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -214,9 +252,11 @@ def bench_act(args):
     avg_launch_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
     nbytes = act_bytes(rows, cols, G, transpose)
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    if args.copy_probe:
+        copy_probe()
     print(f"[bench] {args.steps} timed calls: {ms_per_step * 1e3:.1f} us/call wall, "
           f"avg launch {avg_launch_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    traffic = traffic_from_profile(nbytes, PMC_SUMMARY_ACT) if transpose else None
+    traffic = traffic_from_profile(nbytes, PMC_SUMMARY_ACT, ACT_SOURCES) if transpose else None
     rec = {
         "metric": "Gelem/s per per-group E4M3 activation quantization (codes + transposed "
                   "codes) + achieved HBM GB/s (% of peak), 1 GPU",
@@ -234,6 +274,7 @@ def bench_act(args):
         "config": {
             "workload": f"activation {rows}x{cols} BF16 (tokens x channels), 1x{G} groups, "
                         f"E4M3 codes{' + transposed codes' if transpose else ''} + FP32 scales",
+            "buffer_sets": nset,
             "group_size": G,
             "algorithmic_bytes_per_step": nbytes,
         },
@@ -317,14 +358,7 @@ def main():
           file=sys.stderr, flush=True)
 
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")  # 4 GiB
-        dst = torch.empty_like(src)
-        src.fill_(1.0)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print("[bench] copy probe: 3 x 4 GiB device copies done", file=sys.stderr, flush=True)
-        del src, dst
+        copy_probe()
 
     traffic = traffic_from_profile(bytes_per_launch)
     value = n_params / (ms_per_step * 1e-3) / 1e9

@@ -165,7 +165,7 @@ coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x,
  * rows is a multiple of 16, bytes otherwise.
  * Errors: NULL_POINTER (x/codes/scales NULL with rows, cols > 0),
  * INVALID_VALUE (rows or cols < 0, cols % group_size != 0, more than 2^31-1
- * tiles of 64 x 128), GROUP_SIZE, MISALIGNED, HIP.
+ * tiles of 128 x 128), GROUP_SIZE, MISALIGNED, HIP.
  */
 coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows,
                                     int64_t cols, int32_t group_size,

@@ -194,6 +194,28 @@ def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):
                       f"{dt:.2f} s wall"}
 
 
+def copy_ceiling_gbps(reps: int = 5) -> float:
+    """Median rate of a plain 4 GiB device-to-device copy (read + write bytes
+    over time): the streaming ceiling of this GPU, for context."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    dst.copy_(src)
+    rates = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        rates.append(2 * src.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del src, dst
+    torch.cuda.synchronize()
+    return sorted(rates)[len(rates) // 2]
+
+
 def copy_probe():
     """Three 4 GiB device-to-device copies: a kernel of known traffic against
     which the profiler's FETCH_SIZE / WRITE_SIZE counters are scaled."""
@@ -250,8 +272,10 @@ def bench_act(args):
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     avg_launch_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
+    launch_sorted = sorted(a.elapsed_time(b) for a, b in events)
     nbytes = act_bytes(rows, cols, G, transpose)
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    ceiling = copy_ceiling_gbps()
     if args.copy_probe:
         copy_probe()
     print(f"[bench] {args.steps} timed calls: {ms_per_step * 1e3:.1f} us/call wall, "
@@ -277,6 +301,10 @@ def bench_act(args):
             "buffer_sets": nset,
             "group_size": G,
             "algorithmic_bytes_per_step": nbytes,
+            "launch_ms_median": round(launch_sorted[len(launch_sorted) // 2], 5),
+            "launch_ms_min": round(launch_sorted[0], 5),
+            "copy_ceiling_GBps": round(ceiling, 1),
+            "kernel_frac_of_copy_ceiling": round(achieved / ceiling, 4),
         },
         "roofline": {
             "bound": "hbm",
@@ -350,6 +378,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     launch_ms = [[events[k][j][0].elapsed_time(events[k][j][1]) for j in range(len(call_lists))]
                  for k in range(args.steps)]
+    step_ms = sorted(events[k][0][0].elapsed_time(events[k][-1][1]) for k in range(args.steps))
     avg_launch_ms = sum(sum(r) for r in launch_ms) / (args.steps * len(call_lists))
     bytes_per_launch = sum(call_bytes) / len(call_lists)
     achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
@@ -362,6 +391,7 @@ def main():
 
     traffic = traffic_from_profile(bytes_per_launch)
     value = n_params / (ms_per_step * 1e-3) / 1e9
+    ceiling = copy_ceiling_gbps()
     total_bytes = sum(call_bytes)
     rec = {
         "metric": "Gparam/s per fused FP8-AdamW step + achieved HBM GB/s (% of peak), 1 GPU",
@@ -385,6 +415,10 @@ def main():
             "step_frac_of_peak": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_step": total_bytes,
             "launches_per_step": len(call_lists),
+            "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+            "step_ms_min": round(step_ms[0], 4),
+            "copy_ceiling_GBps": round(ceiling, 1),
+            "kernel_frac_of_copy_ceiling": round(achieved / ceiling, 4),
         },
         "roofline": {
             "bound": "hbm",

@@ -65,6 +65,41 @@ def test_encode_dense_sweep_bit_exact():
         assert np.all((got[zero] & 0x7F) == 0)
 
 
+def test_encode_exhaustive_fp32_range():
+    """Every FP32 bit pattern in [-448, 448] (2.28e9 values) through the GPU
+    cast equals the oracle's RNE encoder; -0.0 may give 0x80 or 0x00."""
+    import concurrent.futures as cf
+    coat = lib()
+    end = 0x43E00001                      # bits of 448.0, inclusive
+    chunk = 1 << 26
+    codes = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    pool = cf.ThreadPoolExecutor(8)
+
+    def host_ref(bits_np):
+        parts = np.array_split(bits_np, 8)
+        return np.concatenate(list(pool.map(
+            lambda b: oracle.e4m3_encode_array(b.view(np.float32).astype(np.float64)), parts)))
+
+    for sign in (0, 1):
+        for start in range(0, end, chunk):
+            stop = min(end, start + chunk)
+            bits = torch.arange(start, stop, dtype=torch.int32, device=DEV)
+            if sign:
+                bits = bits + torch.iinfo(torch.int32).min       # set bit 31
+            c = codes[:stop - start]
+            coat.e4m3_encode(bits.view(torch.float32), c)
+            got = c.cpu().numpy()
+            hb = np.arange(start, stop, dtype=np.uint32) | np.uint32(sign << 31)
+            ref = host_ref(hb)
+            if start == 0:                                    # +-0.0
+                assert (got[0] & 0x7F) == 0 and ref[0] == 0
+                got, ref = got[1:], ref[1:]
+            bad = np.flatnonzero(got != ref)
+            assert bad.size == 0, (sign, start, bad[:4], got[bad[:4]], ref[bad[:4]])
+    pool.shutdown()
+    print("[codec] exhaustive FP32 [-448, 448] sweep bit-exact", flush=True)
+
+
 def _random_groups(rng, n, G, spreads):
     x = np.empty(n, np.float32)
     for g0 in range(0, n, G):

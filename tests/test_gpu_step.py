@@ -102,6 +102,39 @@ def test_deterministic_and_stream_ordered():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+def test_resume_through_host_equals_straight_run():
+    """5 steps, the whole state copied to the host and into fresh device
+    buffers, 5 more steps: bitwise equal to 10 straight steps (the state is
+    complete: codes, scale, k and w; the step count is the caller's)."""
+    coat = lib()
+    n, G = 200_000 + 77, 128
+
+    def fresh():
+        return (inputs.weights(n, 0, DEV), coat.QuantState.zeros(n, G, DEV),
+                coat.QuantState.zeros(n, G, DEV))
+
+    def steps(w, m, v, ts):
+        for t in ts:
+            g = inputs.gradient(n, 1e-3, t, 0, DEV)
+            coat.adamw_fp8_step([coat.ParamSlot(w, g, m, v)], **HP, step=t, group_size=G)
+        torch.cuda.synchronize()
+
+    w, m, v = fresh()
+    steps(w, m, v, range(1, 11))
+    a = [x.cpu().numpy() for x in (w, m.codes, m.scale, m.k, v.codes, v.scale, v.k)]
+    w, m, v = fresh()
+    steps(w, m, v, range(1, 6))
+    host = [x.cpu().numpy().copy() for x in (w, m.codes, m.scale, m.k, v.codes, v.scale, v.k)]
+    del w, m, v
+    w = torch.from_numpy(host[0]).to(DEV)
+    m = coat.QuantState(*[torch.from_numpy(h).to(DEV) for h in host[1:4]])
+    v = coat.QuantState(*[torch.from_numpy(h).to(DEV) for h in host[4:7]])
+    steps(w, m, v, range(6, 11))
+    b = [x.cpu().numpy() for x in (w, m.codes, m.scale, m.k, v.codes, v.scale, v.k)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
 def test_free_running_drift_report():
     """GPU and oracle each run 10 steps on their own from zero state.  Not a
     parity gate: each side's rounding feeds its next step, and the first

@@ -57,6 +57,10 @@ def _lib():
         lib.coat_oracle_quantize_act.restype = ctypes.c_int
         lib.coat_oracle_quantize_act.argtypes = [
             _u16p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _u8p, _f32p, _vp]
+        lib.coat_oracle_gemm_fp8_group_quant.restype = ctypes.c_int
+        lib.coat_oracle_gemm_fp8_group_quant.argtypes = [
+            _u8p, _u8p, ctypes.c_float, ctypes.c_float, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int32, _u8p, _f32p, _vp, _vp]
         _LIB = lib
     return _LIB
 
@@ -181,3 +185,25 @@ def quantize_act(x_bf16_bits, rows, cols, group_size, transpose=True):
                                            _ptr(codes_t)), "quantize_act")
     return (codes.reshape(rows, cols), scales.reshape(rows, cols // group_size),
             None if codes_t is None else codes_t.reshape(cols, rows))
+
+
+def gemm_fp8_group_quant(a_codes, b_codes, a_scale, b_scale, group_size, want_c=False):
+    """Group-scaled FP8 linear layer: C = a_scale * b_scale * A B^T with A
+    (M x K) and B (N x K) given as E4M3 codes, quantized per 1 x group_size
+    group of each row of C.  Returns (codes[M, N], scales[M, N // G]) and,
+    with want_c, also (c_exact float64[M, N], c_f32 float32[M, N])."""
+    a = np.ascontiguousarray(a_codes, dtype=np.uint8)
+    b = np.ascontiguousarray(b_codes, dtype=np.uint8)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    codes = np.zeros((M, N), np.uint8)
+    scales = np.zeros((M, N // group_size if group_size else 0), np.float32)
+    c64 = np.zeros((M, N), np.float64) if want_c else None
+    c32 = np.zeros((M, N), np.float32) if want_c else None
+    _check(_lib().coat_oracle_gemm_fp8_group_quant(
+        a, b, a_scale, b_scale, M, N, K, group_size, codes, scales, _ptr(c64), _ptr(c32)),
+        "gemm_fp8_group_quant")
+    if want_c:
+        return codes, scales, c64, c32
+    return codes, scales

@@ -308,41 +308,104 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
 
 /* [P1] eq. FP8量化 on each 1xG group of a row: S = max|X| / 448 and
  * X_FP8 = round(X / S), evaluated as x * (448 / max) in FP32. */
+/* One 1xG group of FP32 values through [P1] eq. FP8量化 with S = max|x| / 448.
+ * Reading: the rounding decisions are taken in FP32, r = 448 / max and
+ * q = x * r each rounded to FP32, code = RNE_E4M3(q); the stored scale is
+ * S = max / 448 (IEEE division).  An all-zero group stores S = 0 and codes 0.
+ * Below 2^-100, 448 / max would overflow FP32's exponent range, so such
+ * groups scale max and x by 2^64 first (exact; the rounded results are those
+ * of an FP32 with unbounded exponent). */
+static void quantize_group_e4m3(const float* x, int64_t len, uint8_t* codes, float* scale) {
+  float amax = 0.0f;
+  for (int64_t j = 0; j < len; ++j) {
+    const float a = fabsf(x[j]);
+    if (a > amax) amax = a;
+  }
+  if (amax == 0.0f) {
+    *scale = 0.0f;
+    for (int64_t j = 0; j < len; ++j) codes[j] = 0x00;
+    return;
+  }
+  const int tiny = amax < 0x1p-100f;
+  const float pre = tiny ? 0x1p64f : 1.0f;
+  const float r = (float)kE4M3Max / (amax * pre);
+  *scale = amax / (float)kE4M3Max;
+  for (int64_t j = 0; j < len; ++j) {
+    const float q = (x[j] * pre) * r;
+    codes[j] = coat_oracle_e4m3_encode((double)q);
+  }
+}
+
 int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                              int32_t group_size, uint8_t* codes, float* scales,
                              uint8_t* codes_t) {
   if (rows < 0 || cols < 0 || group_size < 1 || cols % group_size != 0)
     return COAT_ORACLE_EINVAL;
   const int64_t groups_per_row = cols / group_size;
+  float* row = malloc(sizeof(float) * (size_t)(cols > 0 ? cols : 1));
+  if (!row) return COAT_ORACLE_ENOMEM;
   for (int64_t i = 0; i < rows; ++i) {
-    for (int64_t gj = 0; gj < groups_per_row; ++gj) {
-      const int64_t c0 = gj * group_size;
-      float amax = 0.0f;
-      for (int64_t j = c0; j < c0 + group_size; ++j) {
-        const float a = fabsf(bf16_to_float(x_bf16[i * cols + j]));
-        if (a > amax) amax = a;
-      }
-      if (amax == 0.0f) {
-        scales[i * groups_per_row + gj] = 0.0f;
-        for (int64_t j = c0; j < c0 + group_size; ++j) codes[i * cols + j] = 0x00;
-        continue;
-      }
-      /* r = 448 / max and q = x * r, each rounded to FP32.  Below 2^-100 the
-       * quotient would overflow FP32's exponent range, so such groups scale
-       * max and x by 2^64 first (exact; the rounded results are those of an
-       * FP32 with unbounded exponent). */
-      const int tiny = amax < 0x1p-100f;
-      const float pre = tiny ? 0x1p64f : 1.0f;
-      const float r = (float)kE4M3Max / (amax * pre);
-      scales[i * groups_per_row + gj] = amax / (float)kE4M3Max;
-      for (int64_t j = c0; j < c0 + group_size; ++j) {
-        const float q = (bf16_to_float(x_bf16[i * cols + j]) * pre) * r;
-        codes[i * cols + j] = coat_oracle_e4m3_encode((double)q);
-      }
-    }
+    for (int64_t j = 0; j < cols; ++j) row[j] = bf16_to_float(x_bf16[i * cols + j]);
+    for (int64_t gj = 0; gj < groups_per_row; ++gj)
+      quantize_group_e4m3(row + gj * group_size, group_size, codes + i * cols + gj * group_size,
+                          scales + i * groups_per_row + gj);
   }
+  free(row);
   if (codes_t)
     for (int64_t i = 0; i < rows; ++i)
       for (int64_t j = 0; j < cols; ++j) codes_t[j * rows + i] = codes[i * cols + j];
+  return COAT_ORACLE_OK;
+}
+
+/* ------------------------------------------- group-scaled FP8 linear layer */
+
+/* E4M3 value of a code in units of 2^-9, the smallest subnormal: every finite
+ * E4M3 value is an integer multiple of it, so products of two such integers
+ * and their sums are exact in int64. */
+static int32_t e4m3_units(uint8_t code) {
+  return (int32_t)(coat_oracle_e4m3_decode(code) * 512.0);
+}
+
+int coat_oracle_gemm_fp8_group_quant(const uint8_t* a, const uint8_t* b, float a_scale,
+                                     float b_scale, int64_t M, int64_t N, int64_t K,
+                                     int32_t group_size, uint8_t* codes, float* scales,
+                                     double* c_exact, float* c_f32) {
+  if (M < 0 || N < 0 || K < 0 || K > (1 << 17) || group_size < 1 || N % group_size != 0)
+    return COAT_ORACLE_EINVAL;
+  for (int64_t i = 0; i < M * K; ++i)
+    if ((a[i] & 0x7F) == 0x7F) return COAT_ORACLE_ESTATE;
+  for (int64_t i = 0; i < N * K; ++i)
+    if ((b[i] & 0x7F) == 0x7F) return COAT_ORACLE_ESTATE;
+  int32_t* ia = malloc(sizeof(int32_t) * (size_t)(M * K > 0 ? M * K : 1));
+  int32_t* ib = malloc(sizeof(int32_t) * (size_t)(N * K > 0 ? N * K : 1));
+  float* row = malloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+  if (!ia || !ib || !row) {
+    free(ia);
+    free(ib);
+    free(row);
+    return COAT_ORACLE_ENOMEM;
+  }
+  for (int64_t i = 0; i < M * K; ++i) ia[i] = e4m3_units(a[i]);
+  for (int64_t i = 0; i < N * K; ++i) ib[i] = e4m3_units(b[i]);
+  const double scale = (double)a_scale * (double)b_scale;  /* exact: 24 + 24 bits */
+  const int64_t groups_per_row = N / group_size;
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t j = 0; j < N; ++j) {
+      /* C = A B^T: the sum over k is exact (|sum| < K * 2^36 <= 2^53). */
+      int64_t acc = 0;
+      for (int64_t k = 0; k < K; ++k) acc += (int64_t)ia[i * K + k] * ib[j * K + k];
+      const double c = (double)acc * 0x1p-18 * scale;
+      if (c_exact) c_exact[i * N + j] = c;
+      row[j] = (float)c;
+    }
+    if (c_f32)
+      for (int64_t j = 0; j < N; ++j) c_f32[i * N + j] = row[j];
+    for (int64_t gj = 0; gj < groups_per_row; ++gj)
+      quantize_group_e4m3(row + gj * group_size, group_size, codes + i * N + gj * group_size,
+                          scales + i * groups_per_row + gj);
+  }
+  free(ia);
+  free(ib);
+  free(row);
   return COAT_ORACLE_OK;
 }

@@ -49,6 +49,7 @@ extern "C" {
 #define COAT_ORACLE_OK 0
 #define COAT_ORACLE_EINVAL 1   /* bad size, group size or hyperparameter */
 #define COAT_ORACLE_ESTATE 2   /* state holds a NaN code or a nonpositive k */
+#define COAT_ORACLE_ENOMEM 3   /* a scratch allocation failed */
 
 /* [OCP] value of one E4M3 code (NaN for 0x7F / 0xFF). */
 double coat_oracle_e4m3_decode(uint8_t code);
@@ -104,6 +105,21 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
 int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
                              int32_t group_size, uint8_t* codes, float* scales,
                              uint8_t* codes_t);
+
+/* Group-scaled FP8 linear layer ([P1] section 三, Triton优化内核 / 线性层优化:
+ * the GEMM output is reshaped into 1xG groups along N and each group's max is
+ * taken; section 四 table, 组缩放技术).  C = (a_scale * b_scale) * A B^T with
+ * A: M x K and B: N x K E4M3 codes, row-major (K contiguous).  Reading: C is
+ * the real product (the sum over k is exact in integer arithmetic, the scale
+ * is applied in double) rounded to FP32, and its 1xG groups along each row go
+ * through the same FP32 quantizer as the activation quantizer above.
+ * codes: M x N, scales: M x N/G; c_exact (M x N doubles) and c_f32 (M x N)
+ * are optional (NULL to skip).  K <= 2^17; N a multiple of group_size; NaN
+ * codes in A or B give COAT_ORACLE_ESTATE. */
+int coat_oracle_gemm_fp8_group_quant(const uint8_t* a, const uint8_t* b, float a_scale,
+                                     float b_scale, int64_t M, int64_t N, int64_t K,
+                                     int32_t group_size, uint8_t* codes, float* scales,
+                                     double* c_exact, float* c_f32);
 
 #ifdef __cplusplus
 }

@@ -88,6 +88,22 @@ static int run_act(int64_t rows, int64_t cols, int32_t G) {
   return 0;
 }
 
+static int run_gemm(int64_t M, int64_t N, int64_t K, int32_t G) {
+  uint8_t* a = malloc((size_t)(M * K + 1));
+  uint8_t* b = malloc((size_t)(N * K + 1));
+  uint8_t* c = malloc((size_t)(M * N + 1));
+  float* s = malloc(sizeof(float) * (size_t)(M * (N / G) + 1));
+  double* c64 = malloc(sizeof(double) * (size_t)(M * N + 1));
+  float* c32 = malloc(sizeof(float) * (size_t)(M * N + 1));
+  if (!a || !b || !c || !s || !c64 || !c32) return 1;
+  for (int64_t i = 0; i < M * K; ++i) a[i] = (uint8_t)(urand() * 126.0) | (urand() < 0.5 ? 0x80 : 0);
+  for (int64_t i = 0; i < N * K; ++i) b[i] = (uint8_t)(urand() * 126.0) | (urand() < 0.5 ? 0x80 : 0);
+  CHECK(coat_oracle_gemm_fp8_group_quant(a, b, 0.5f, 3.0f, M, N, K, G, c, s, c64, c32));
+  CHECK(coat_oracle_gemm_fp8_group_quant(a, b, 0.5f, 3.0f, M, N, K, G, c, s, NULL, NULL));
+  free(a); free(b); free(c); free(s); free(c64); free(c32);
+  return 0;
+}
+
 int main(void) {
   static const int64_t sizes[] = {1, 17, 127, 128, 129, 1000, 4096 + 5};
   static const int32_t groups[] = {16, 32, 64, 128};
@@ -95,6 +111,7 @@ int main(void) {
     for (size_t si = 0; si < sizeof sizes / sizeof sizes[0]; ++si)
       if (run_size(sizes[si], groups[gi])) return 1;
     if (run_act(3, 2 * groups[gi], groups[gi]) || run_act(37, groups[gi], groups[gi])) return 1;
+    if (run_gemm(5, 2 * groups[gi], 17, groups[gi]) || run_gemm(1, groups[gi], 1, groups[gi])) return 1;
   }
   double xs[300];
   uint8_t cs[300];

@@ -1,0 +1,104 @@
+"""Pins of the oracle's group-scaled FP8 linear layer (COAT review, section 三
+"Triton优化内核" / linear-layer kernels: output reshaped into 1xG groups whose
+max is taken; section 四 table, group scaling).
+
+Pinned by: exact rational arithmetic on small cases (brute force with
+fractions), closed forms (an identity-like A copies B^T), the transpose and
+scale laws, torch's FP8 cast of the FP32 products for the quantization step,
+and rejection of NaN codes and ragged groups."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+E4M3_ONE = 0x38
+
+
+def _rand_codes(rng, shape, finite_only=True):
+    c = rng.integers(0, 256, shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x7E           # no NaN codes
+    return c
+
+
+def _dec(codes):
+    return oracle.e4m3_decode_array(np.ascontiguousarray(codes).ravel()).reshape(codes.shape)
+
+
+def test_exact_against_rational_brute_force():
+    rng = np.random.default_rng(0)
+    M, N, K, G = 3, 32, 9, 16
+    a, b = _rand_codes(rng, (M, K)), _rand_codes(rng, (N, K))
+    sa, sb = 0.375, 1.25
+    _, _, c64, c32 = oracle.gemm_fp8_group_quant(a, b, sa, sb, G, want_c=True)
+    fa = [[Fraction(float(v)) for v in row] for row in _dec(a)]
+    fb = [[Fraction(float(v)) for v in row] for row in _dec(b)]
+    for i in range(M):
+        for j in range(N):
+            exact = Fraction(sa) * Fraction(sb) * sum(x * y for x, y in zip(fa[i], fb[j]))
+            assert c64[i, j] == float(exact)                 # exact here (few terms)
+            assert c32[i, j] == np.float32(float(exact))
+
+
+def test_identity_like_a_copies_b():
+    rng = np.random.default_rng(1)
+    N, K, G = 64, 64, 32
+    a = np.zeros((K, K), np.uint8)
+    a[np.arange(K), np.arange(K)] = E4M3_ONE                # A = I (as E4M3 ones)
+    b = _rand_codes(rng, (N, K))
+    _, _, c64, _ = oracle.gemm_fp8_group_quant(a, b, 2.0, 0.5, G, want_c=True)
+    assert np.array_equal(c64, _dec(b).T)                    # C = A B^T = B^T
+
+
+def test_transpose_and_scale_laws():
+    rng = np.random.default_rng(2)
+    M, N, K, G = 16, 48, 40, 16
+    a, b = _rand_codes(rng, (M, K)), _rand_codes(rng, (N, K))
+    codes, scales, c64, _ = oracle.gemm_fp8_group_quant(a, b, 1.0, 1.0, G, want_c=True)
+    _, _, c64t, _ = oracle.gemm_fp8_group_quant(b, a, 1.0, 1.0, G, want_c=True)
+    assert np.array_equal(c64, c64t.T)
+    codes8, scales8, c64s, _ = oracle.gemm_fp8_group_quant(a, b, 8.0, 0.25, G, want_c=True)
+    assert np.array_equal(c64s, 2.0 * c64)                   # power-of-two scales are exact
+    assert np.array_equal(codes8, codes)                     # codes are scale invariant
+    assert np.array_equal(scales8, 2.0 * scales)
+
+
+@pytest.mark.parametrize("G", [16, 32, 64, 128])
+def test_quantization_matches_torch_cast(G):
+    rng = np.random.default_rng(3)
+    M, N, K = 9, 2 * G, 96
+    a, b = _rand_codes(rng, (M, K)), _rand_codes(rng, (N, K))
+    codes, scales, _, c32 = oracle.gemm_fp8_group_quant(a, b, 0.01, 0.02, G, want_c=True)
+    x = torch.from_numpy(c32).reshape(M, N // G, G)
+    amax = x.abs().amax(-1, keepdim=True)
+    r = torch.tensor(448.0, dtype=torch.float32) / amax
+    ref = (x * r).reshape(M, N).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nz = (c32 != 0)                                          # torch keeps -0's sign
+    assert np.array_equal(codes[nz], ref[nz])
+    assert np.array_equal(scales, (amax / 448.0).reshape(M, N // G).numpy())
+
+
+def test_matches_float64_matmul_of_decoded_values():
+    rng = np.random.default_rng(4)
+    M, N, K, G = 20, 64, 256, 64
+    a, b = _rand_codes(rng, (M, K)), _rand_codes(rng, (N, K))
+    _, _, c64, _ = oracle.gemm_fp8_group_quant(a, b, 1.0, 1.0, G, want_c=True)
+    ref = _dec(a) @ _dec(b).T
+    assert np.allclose(c64, ref, rtol=1e-12, atol=1e-9)
+
+
+def test_zero_rows_nan_codes_and_ragged_groups():
+    rng = np.random.default_rng(5)
+    a = _rand_codes(rng, (4, 32))
+    a[2] = 0
+    b = _rand_codes(rng, (32, 32))
+    codes, scales = oracle.gemm_fp8_group_quant(a, b, 1.0, 1.0, 16)
+    assert not codes[2].any() and not scales[2].any()
+    bad = a.copy()
+    bad[0, 0] = 0x7F
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm_fp8_group_quant(bad, b, 1.0, 1.0, 16)
+    with pytest.raises(oracle.OracleError):
+        oracle.gemm_fp8_group_quant(a, b[:24], 1.0, 1.0, 16)     # N = 24 not a multiple of G

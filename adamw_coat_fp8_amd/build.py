@@ -8,7 +8,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("coat_fp8.hip", "coat_act.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("coat_fp8.hip", "coat_act.hip", "coat_gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcoat_fp8.so")
 ARCH = "gfx950"

@@ -30,7 +30,8 @@ COAT_ERR_HIP = 5
 
 EXPORTED_SYMBOLS = (
     "coat_adamw_fp8_step", "coat_fp8_expand_quantize", "coat_fp8_dequantize_expand",
-    "coat_e4m3_encode", "coat_e4m3_decode", "coat_fp8_quantize_act", "coat_status_string",
+    "coat_e4m3_encode", "coat_e4m3_decode", "coat_fp8_quantize_act",
+    "coat_fp8_gemm_group_quant", "coat_fp8_gemm_bf16", "coat_status_string",
     "coat_last_hip_error", "coat_abi_version",
 )
 
@@ -77,6 +78,11 @@ def _load(path: str = LIB_PATH):
     lib.coat_e4m3_decode.argtypes = [vp, i64, vp, vp]
     lib.coat_fp8_quantize_act.restype = ctypes.c_int
     lib.coat_fp8_quantize_act.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp]
+    f32 = ctypes.c_float
+    lib.coat_fp8_gemm_group_quant.restype = ctypes.c_int
+    lib.coat_fp8_gemm_group_quant.argtypes = [vp, vp, f32, f32, i64, i64, i64, i32, vp, vp, vp, vp]
+    lib.coat_fp8_gemm_bf16.restype = ctypes.c_int
+    lib.coat_fp8_gemm_bf16.argtypes = [vp, vp, f32, f32, i64, i64, i64, vp, vp]
     lib.coat_status_string.restype = ctypes.c_char_p
     lib.coat_status_string.argtypes = [ctypes.c_int]
     lib.coat_last_hip_error.restype = ctypes.c_char_p
@@ -213,3 +219,29 @@ def quantize_act(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     rows, cols = x.shape
     _check(lib.coat_fp8_quantize_act(_ptr(x), rows, cols, group_size, _ptr(codes),
                                      _ptr(scales), _ptr(codes_t), _stream(stream)))
+
+
+def gemm_group_quant(a: torch.Tensor, b: torch.Tensor, a_scale: float, b_scale: float,
+                     codes: torch.Tensor, scales: torch.Tensor, group_size: int = 128,
+                     c_f32: Optional[torch.Tensor] = None, stream=None):
+    """C = a_scale * b_scale * a @ b.T from E4M3 codes a (M x K) and b (N x K),
+    quantized per 1 x group_size group of each row into codes (M x N) and
+    scales (M x N/group_size); optionally also writes C in FP32."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    _check(lib.coat_fp8_gemm_group_quant(_ptr(a), _ptr(b), a_scale, b_scale, M, N, K,
+                                         group_size, _ptr(codes), _ptr(scales), _ptr(c_f32),
+                                         _stream(stream)))
+
+
+def gemm_bf16(a: torch.Tensor, b: torch.Tensor, a_scale: float, b_scale: float,
+              c_bf16: torch.Tensor, stream=None):
+    """C = a_scale * b_scale * a @ b.T from E4M3 codes, rounded to BF16."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    _check(lib.coat_fp8_gemm_bf16(_ptr(a), _ptr(b), a_scale, b_scale, M, N, K, _ptr(c_bf16),
+                                  _stream(stream)))

@@ -1,0 +1,385 @@
+// coat_gemm.hip -- gfx950 FP8 GEMM with a group-scaled FP8 epilogue (COAT's
+// linear-layer output quantization) and the same GEMM with a plain BF16
+// epilogue, plus their C ABI.
+//
+// Sources (see include/coat_fp8.h for the full citations):
+//   [P1] COAT paper review (xllm-io.github.io), section 三, Triton优化内核 /
+//        线性层优化: the GEMM output is viewed as (BLOCK_M, BLOCK_N/G, G) and
+//        the max is taken along the last axis; section 四 table, 组缩放技术:
+//        a two-stage max reduction fused into the producing operation;
+//        核心公式 "FP8量化" for the per-group quantizer.
+//   [OCP] OFP8 specification, E4M3.
+//
+// Execution model.  C = s * A B^T with A (M x K) and B (N x K) E4M3 codes,
+// row-major, s = a_scale * b_scale.  A 256-thread block computes a 128 x 128
+// tile of C; its four waves each own 64 x 64 as 2 x 2 tiles of the 32x32x64
+// FP8 MFMA, accumulating in FP32.  K advances 128 at a time through a double
+// buffered LDS copy of the A and B panels, loaded straight from global memory
+// into LDS (16-byte chunks XOR-swizzled by row, so the MFMA operand reads are
+// free of bank conflicts) while the MFMAs of the previous panels run.  In the 32x32 MFMA result a row's 32 columns lie across
+// the 32 lanes of a half wave, so the epilogue's group max is stage one: DPP
+// inside 16-lane rows, a swizzle across the half wave, a register max across
+// the wave's two column tiles; and, for G = 128, stage two: an exchange of row
+// maxima between the two waves that share rows, through LDS.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <type_traits>
+
+#include "coat_common.h"
+
+using namespace coat;
+
+namespace {
+
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 128;
+constexpr int kPanelBytes = kBM * kBK;  // one A or B panel in LDS: 16 KB
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+enum Epilogue { kGroupQuant = 0, kBF16 = 1 };
+
+struct GemmParams {
+  const uint8_t* a;
+  const uint8_t* b;
+  uint8_t* codes;    // M x N E4M3 (group quant)
+  float* scales;     // M x N/G (group quant)
+  float* c_f32;      // optional M x N FP32 C (group quant)
+  uint16_t* c_bf16;  // M x N BF16 (plain epilogue)
+  int64_t M, N, K;
+  int64_t n_tiles;   // N / 128
+  float scale;       // a_scale * b_scale, rounded to FP32
+};
+
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
+  const int64_t q = nb / 8, r = nb % 8;
+  const int64_t xcd = b % 8, local = b / 8;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Byte offset of 16-byte chunk c of row `row` in a 128-byte-row LDS panel.
+__device__ __forceinline__ int panel_off(int row, int c) { return row * 128 + 16 * (c ^ (row & 7)); }
+
+// Max over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Max with lane ^ 16 inside each 32-lane half (ds_swizzle bit mode, xor 0x10).
+__device__ __forceinline__ float swap16_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+}
+
+// x * r rounded once to FP32, -0 folded to +0 (see the activation quantizer).
+__device__ __forceinline__ float gq_scaled(float x, float r) {
+#pragma clang fp contract(off)
+  return x * r + 0.0f;
+}
+
+__device__ __forceinline__ float scale_acc(float acc, float s) {
+#pragma clang fp contract(off)
+  return acc * s;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int G, int kEpi>
+__global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kPanelBytes];  // A0 B0 A1 B1
+  __shared__ float red[2][kBM];                                          // stage-two maxima
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t tm = bid / p.n_tiles, tn = bid - tm * p.n_tiles;
+  const int64_t m0 = tm * kBM, n0 = tn * kBN;
+  const int64_t K = p.K;
+
+  // Panel loads go straight from global memory into LDS: one wave-wide
+  // 16-byte-per-lane load fills 1 KB, 8 rows of a panel, lane L landing at
+  // byte 16 L.  So lane L carries row R0 + L/8 and the physical chunk L%8,
+  // which under the row swizzle holds logical chunk (L%8) ^ (L/8); the swizzle
+  // is applied on the global side.  Wave w fills rows 32 w .. 32 w + 31 of each
+  // panel with 4 loads.  Rows of A past M are not loaded (their LDS bytes are
+  // stale and only reach output rows that are never stored).
+  const uint8_t* a_blk = p.a + m0 * K;
+  const uint8_t* b_blk = p.b + n0 * K;
+  uint32_t goff[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3);
+    goff[i] = (uint32_t)row * (uint32_t)K + 16u * (uint32_t)c;
+    a_ok[i] = m0 + row < p.M;
+  }
+  auto issue = [&](int64_t k0, int buf) __attribute__((always_inline)) {
+    uint8_t* As = smem + buf * 2 * kPanelBytes;
+    uint8_t* Bs = As + kPanelBytes;
+    const uint8_t* ak = a_blk + k0;
+    const uint8_t* bk = b_blk + k0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint8_t* dst_a = As + 1024 * (4 * wave + i);
+      uint8_t* dst_b = Bs + 1024 * (4 * wave + i);
+      if (a_ok[i]) __builtin_amdgcn_global_load_lds(ak + goff[i], dst_a, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bk + goff[i], dst_b, 16, 0, 0);
+    }
+  };
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / kBK);
+  if (nk > 0) issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int half = lane >> 5, l32 = lane & 31;
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) issue((int64_t)(kt + 1) * kBK, (kt + 1) & 1);
+    const uint8_t* As = smem + (kt & 1) * 2 * kPanelBytes;
+    const uint8_t* Bs = As + kPanelBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // lane supplies row (l32) and k bytes 64 kk + 32 half .. +31: chunks c0, c0 + 1
+      const int c0 = 4 * kk + 2 * half;
+      v8i fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + 32 * i + l32;
+        const uint4 lo = *reinterpret_cast<const uint4*>(As + panel_off(row, c0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(As + panel_off(row, c0 + 1));
+        fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wn * 64 + 32 * j + l32;
+        const uint4 lo = *reinterpret_cast<const uint4*>(Bs + panel_off(row, c0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(Bs + panel_off(row, c0 + 1));
+        fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0,
+                                                                      0, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next panels have landed
+    __syncthreads();
+  }
+
+  // Epilogue.  Value (i, j, r) of this lane is C[row][col] with
+  //   row = wm*64 + 32 i + 8 (r/4) + 4 half + r%4,  col = wn*64 + 32 j + l32.
+  const float s = p.scale;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = scale_acc(acc[i][j][r], s);
+
+  if constexpr (kEpi == kBF16) {
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // 128 x 128 BF16 = 32 KB
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int col = wn * 64 + 32 * j + l32;
+          tile[row * kBN + col] = bf16_rne(acc[i][j][r]);
+        }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = t + kBlockThreads * i, row = q >> 4, c = q & 15;
+      if (m0 + row < p.M) {
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN + 8 * c);
+        *reinterpret_cast<uint4*>(p.c_bf16 + (m0 + row) * p.N + n0 + 8 * c) = v;
+      }
+    }
+  } else {
+    if (p.c_f32) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (row < p.M) p.c_f32[row * p.N + n0 + wn * 64 + 32 * j + l32] = acc[i][j][r];
+          }
+    }
+    // One row tile (i) at a time, to bound the live registers.
+    uint8_t* tile = smem;
+    const int64_t gpr = p.N / G;
+    // (a compile-time row tile index keeps acc[i] in registers across the barriers)
+    auto row_tile = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      // Stage one: |C| maxima over G columns inside the wave.
+      float gmax[2][16];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = row16_max(fabsf(acc[i][j][r]));
+          if constexpr (G >= 32) v = swap16_max(v);
+          gmax[j][r] = v;
+        }
+      if constexpr (G >= 64) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gmax[0][r] = gmax[1][r] = fmaxf(gmax[0][r], gmax[1][r]);
+      }
+      // Stage two (G = 128): the two waves holding the same rows swap maxima.
+      if constexpr (G == 128) {
+        if (l32 == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            red[wn][wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3)] = gmax[0][r];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          gmax[0][r] = gmax[1][r] =
+              fmaxf(gmax[0][r], red[wn ^ 1][wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3)]);
+        __syncthreads();  // red is reused by the next row tile
+      }
+      // Quantize into the LDS code tile (128 x 128 bytes) and write the scales.
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float amax = gmax[j][r];
+          const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
+          const float rq = 448.0f / (amax * pre);
+          const float q = gq_scaled(acc[i][j][r] * pre, rq);
+          const uint32_t code =
+              amax > 0.0f ? ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFFu) : 0u;
+          const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int col = wn * 64 + 32 * j + l32;
+          tile[row * kBN + col] = (uint8_t)code;
+          if (col % G == 0 && m0 + row < p.M)
+            p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
+        }
+    };
+    row_tile(std::integral_constant<int, 0>{});
+    row_tile(std::integral_constant<int, 1>{});
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = t + kBlockThreads * i, row = q >> 3, c = q & 7;
+      if (m0 + row < p.M) {
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN + 16 * c);
+        *reinterpret_cast<uint4*>(p.codes + (m0 + row) * p.N + n0 + 16 * c) = v;
+      }
+    }
+  }
+}
+
+template <int G>
+const void* gq_fn() {
+  return reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kGroupQuant>);
+}
+
+const void* gemm_kernel_for(int32_t g, int epi) {
+  if (epi == kBF16) return reinterpret_cast<const void*>(&gemm_fp8_kernel<128, kBF16>);
+  switch (g) {
+    case 16: return gq_fn<16>();
+    case 32: return gq_fn<32>();
+    case 64: return gq_fn<64>();
+    default: return gq_fn<128>();
+  }
+}
+
+coat_status_t check_gemm_shape(const uint8_t* a, const uint8_t* b, float a_scale, float b_scale,
+                               int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || N % kBN != 0 || K % kBK != 0 || K > (1 << 24))
+    return COAT_ERR_INVALID_VALUE;
+  if (!isfinite(a_scale) || !isfinite(b_scale)) return COAT_ERR_INVALID_VALUE;
+  if (M == 0 || N == 0) return COAT_OK;
+  if (K > 0 && (!a || !b)) return COAT_ERR_NULL_POINTER;
+  if (!aligned(a, 16) || !aligned(b, 16)) return COAT_ERR_MISALIGNED;
+  const int64_t m_tiles = (M + kBM - 1) / kBM;
+  if (m_tiles > 0x7FFFFFFF / (N / kBN)) return COAT_ERR_INVALID_VALUE;
+  return COAT_OK;
+}
+
+hipError_t launch_gemm(GemmParams& p, int32_t group_size, int epi, hipStream_t stream) {
+  p.n_tiles = p.N / kBN;
+  const int64_t blocks = (p.M + kBM - 1) / kBM * p.n_tiles;
+  void* args[] = {&p};
+  return hipLaunchKernel(gemm_kernel_for(group_size, epi), dim3((unsigned)blocks),
+                         dim3(kBlockThreads), args, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+coat_status_t coat_fp8_gemm_group_quant(const uint8_t* a, const uint8_t* b, float a_scale,
+                                        float b_scale, int64_t M, int64_t N, int64_t K,
+                                        int32_t group_size, uint8_t* codes, float* scales,
+                                        float* c_f32, hipStream_t stream) {
+  if (!valid_group_size(group_size)) return COAT_ERR_GROUP_SIZE;
+  coat_status_t st = check_gemm_shape(a, b, a_scale, b_scale, M, N, K);
+  if (st != COAT_OK || M == 0 || N == 0) return st;
+  if (!codes || !scales) return COAT_ERR_NULL_POINTER;
+  if (!aligned(codes, 16) || !aligned(scales, 4) || (c_f32 && !aligned(c_f32, 16)))
+    return COAT_ERR_MISALIGNED;
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = a;
+  p.b = b;
+  p.codes = codes;
+  p.scales = scales;
+  p.c_f32 = c_f32;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.scale = (float)((double)a_scale * (double)b_scale);
+  const hipError_t e = launch_gemm(p, group_size, kGroupQuant, stream);
+  return e == hipSuccess ? COAT_OK : hip_fail(e);
+}
+
+coat_status_t coat_fp8_gemm_bf16(const uint8_t* a, const uint8_t* b, float a_scale,
+                                 float b_scale, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* c_bf16, hipStream_t stream) {
+  coat_status_t st = check_gemm_shape(a, b, a_scale, b_scale, M, N, K);
+  if (st != COAT_OK || M == 0 || N == 0) return st;
+  if (!c_bf16) return COAT_ERR_NULL_POINTER;
+  if (!aligned(c_bf16, 16)) return COAT_ERR_MISALIGNED;
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.a = a;
+  p.b = b;
+  p.c_bf16 = c_bf16;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.scale = (float)((double)a_scale * (double)b_scale);
+  const hipError_t e = launch_gemm(p, 128, kBF16, stream);
+  return e == hipSuccess ? COAT_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -263,3 +263,45 @@ def activation(rows: int, cols: int, seed: int, device, kind: str = "llm",
     rest = torch.where(u < 0.17, 1e-20, 1e-5)
     x = torch.where(wide, torch.where(lead, sign * 1e30, x * rest), x)
     return x.to(torch.bfloat16)
+
+
+# ------------------------------------------------ FP8 linear-layer operands
+# Inputs of the group-scaled FP8 linear layer: an activation A (M x K) and a
+# weight B (N x K), each already quantized per tensor to E4M3 codes.
+
+E4M3_SMALL_INTS = (0x00, 0x38, 0x40, 0x44, 0x48, 0x4C, 0x50)   # 0, 1, 2, 3, 4, 6, 8
+
+
+def fp8_operands(M: int, N: int, K: int, seed: int, device, kind: str = "llm"):
+    """Returns (a_codes uint8 M x K, b_codes uint8 N x K, a_scale, b_scale).
+
+    ``llm``: A is ``activation(M, K)`` (N(0, 1) with outlier channels) and B
+    is N(0, 0.02); each is scaled by max|x| / 448 and cast to E4M3 (nearest
+    even), the per-tensor quantization of linear-layer inputs.
+
+    ``exact``: codes of the integers 0, +-1, +-2, +-3, +-4, +-6, +-8 with
+    scales 2^-3 and 2^1, so every product sum is an integer below 2^24 for
+    K <= 2^18 and C is exact in FP32 whatever the summation order."""
+    if kind == "exact":
+        gen = generator(device, _seed(seed, 41, M, N, K))
+        table = torch.tensor(E4M3_SMALL_INTS, dtype=torch.uint8, device=device)
+        def draw(rows):
+            idx = torch.randint(0, len(E4M3_SMALL_INTS), (rows, K), generator=gen, device=device)
+            sign = torch.randint(0, 2, (rows, K), generator=gen, device=device, dtype=torch.uint8)
+            return table[idx] | (sign << 7) * (table[idx] != 0)
+        return draw(M).contiguous(), draw(N).contiguous(), 0.125, 2.0
+    if kind != "llm":
+        raise KeyError(kind)
+    x = activation(M, K, seed, device, "llm", 16).float() if K % 16 == 0 else None
+    if x is None:
+        raise ValueError("K must be a multiple of 16")
+    w = torch.randn(N, K, generator=generator(device, _seed(seed, 42, N, K)), device=device,
+                    dtype=torch.float32) * WEIGHT_STD
+    def quant(t):
+        s = float(t.abs().max()) / 448.0
+        if s == 0.0:
+            s = 1.0
+        return (t / s).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), s
+    a, sa = quant(x)
+    b, sb = quant(w)
+    return a, b, sa, sb

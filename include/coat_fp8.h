@@ -172,6 +172,49 @@ coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows,
                                     uint8_t* codes, float* scales,
                                     uint8_t* codes_t, hipStream_t stream);
 
+/*
+ * Group-scaled FP8 linear layer ([P1] section 三, Triton优化内核 / 线性层优化:
+ * the GEMM output viewed as (BLOCK_M, BLOCK_N/G, G) with the max taken along
+ * the last axis; section 四 table, 组缩放技术: a two-stage max reduction fused
+ * into the producing operation; [P1] 核心公式 FP8量化 with S = max|X| / 448).
+ *   C = (a_scale * b_scale) * A B^T, accumulated in FP32 on the matrix cores,
+ *   then each 1xG group of a row of C is quantized like coat_fp8_quantize_act
+ *   does (r = 448 / max and C * r rounded to FP32, RNE to E4M3, -0 -> 0x00,
+ *   all-zero group -> S = 0 and codes 0).
+ *   a        M x K E4M3 codes, row-major (read only).
+ *   b        N x K E4M3 codes, row-major (read only): the weight of a linear
+ *            layer y = x W^T in its usual [out, in] layout.
+ *   a_scale, b_scale  per-tensor scales, finite; their product is rounded to
+ *            FP32 once and multiplies the FP32 accumulators.
+ *   codes    M x N E4M3 codes, row-major (written).
+ *   scales   M x (N / group_size) FP32, row-major (written).
+ *   c_f32    optional M x N FP32 C before quantization (written), or NULL.
+ * N and K must be multiples of 128, K <= 2^24; M is any size >= 0 (M or N
+ * zero is a no-op; K zero gives C = 0, and a, b may then be NULL).  a, b,
+ * codes and c_f32 16-byte aligned, scales 4-byte aligned.  NaN codes in a or
+ * b are outside the contract.
+ * Errors: NULL_POINTER, INVALID_VALUE (negative sizes, N or K not a multiple
+ * of 128, K > 2^24, non-finite scales, grid too large), GROUP_SIZE,
+ * MISALIGNED, HIP.
+ */
+coat_status_t coat_fp8_gemm_group_quant(const uint8_t* a, const uint8_t* b,
+                                        float a_scale, float b_scale,
+                                        int64_t M, int64_t N, int64_t K,
+                                        int32_t group_size, uint8_t* codes,
+                                        float* scales, float* c_f32,
+                                        hipStream_t stream);
+
+/*
+ * The same FP8 GEMM with a plain epilogue: C = (a_scale * b_scale) * A B^T
+ * rounded to BF16 (nearest even), c_bf16 M x N row-major (written).  It is
+ * the reference point for the cost of the group-scaled epilogue above.
+ * Arguments, layout and errors as above (no group_size).
+ */
+coat_status_t coat_fp8_gemm_bf16(const uint8_t* a, const uint8_t* b,
+                                 float a_scale, float b_scale, int64_t M,
+                                 int64_t N, int64_t K, uint16_t* c_bf16,
+                                 hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* coat_status_string(coat_status_t status);
 

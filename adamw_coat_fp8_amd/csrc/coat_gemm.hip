@@ -17,18 +17,16 @@
 // buffered LDS copy of the A and B panels, loaded straight from global memory
 // into LDS (16-byte chunks XOR-swizzled by row, so the MFMA operand reads are
 // free of bank conflicts) while the MFMAs of the previous panels run.  In the 32x32 MFMA result a row's 32 columns lie across
-// the 32 lanes of a half wave, so the epilogue's group max is stage one: DPP
-// inside 16-lane rows, a swizzle across the half wave, a register max across
-// the wave's two column tiles; and, for G = 128, stage two: an exchange of row
-// maxima between the two waves that share rows, through LDS.
+// the 32 lanes of a half wave; the epilogue therefore stages the scaled FP32
+// tile through LDS and re-reads it row-contiguously, 8 columns per lane, so
+// that the group max is stage one over a lane's 8 values and stage two over
+// the group's G/8 lanes (DPP), with the two divisions per 8 values.
 
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
-
-#include <type_traits>
 
 #include "coat_common.h"
 
@@ -40,6 +38,9 @@ constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kBK = 128;
 constexpr int kPanelBytes = kBM * kBK;  // one A or B panel in LDS: 16 KB
+constexpr int kRowF = kBN + 4;          // padded FP32 row of the epilogue's C tile
+constexpr int kSmemBytes =
+    (4 * kPanelBytes > kBM * kRowF * 4) ? 4 * kPanelBytes : kBM * kRowF * 4;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -68,18 +69,20 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
 // Byte offset of 16-byte chunk c of row `row` in a 128-byte-row LDS panel.
 __device__ __forceinline__ int panel_off(int row, int c) { return row * 128 + 16 * (c ^ (row & 7)); }
 
-// Max over the 16 lanes of a DPP row.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+// Max over the kLanes neighbouring lanes of a group inside a 16-lane DPP row
+// (kLanes a power of two, groups aligned): quad swaps of 1 and 2 lanes, the
+// half-row mirror (joins two quads), the row mirror (joins two halves).
+template <int kLanes>
+__device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
+  if constexpr (kLanes >= 2)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  if constexpr (kLanes >= 4)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  if constexpr (kLanes >= 8)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  if constexpr (kLanes >= 16)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
   return v;
-}
-
-// Max with lane ^ 16 inside each 32-lane half (ds_swizzle bit mode, xor 0x10).
-__device__ __forceinline__ float swap16_max(float v) {
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
 }
 
 // x * r rounded once to FP32, -0 folded to +0 (see the activation quantizer).
@@ -100,8 +103,8 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 template <int G, int kEpi>
 __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kPanelBytes];  // A0 B0 A1 B1
-  __shared__ float red[2][kBM];                                          // stage-two maxima
+  // A0 B0 A1 B1 panels in the main loop; the FP32 C tile in the epilogue
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
@@ -220,78 +223,54 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
       }
     }
   } else {
-    if (p.c_f32) {
+    // The scaled C tile goes to LDS as FP32 (rows padded to 132 floats), and
+    // the quantizer then walks it like the activation quantizer: a thread
+    // takes 8 consecutive columns of a row per pass, so a group of G columns
+    // sits on G/8 neighbouring lanes of a 16-lane DPP row.  Stage one of the
+    // max is the thread's 8 values, stage two the DPP steps across the group's
+    // lanes; the divisions (r and S) are once per 8 values.
+    float* ct = reinterpret_cast<float*>(smem);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (row < p.M) p.c_f32[row * p.N + n0 + wn * 64 + 32 * j + l32] = acc[i][j][r];
-          }
-    }
-    // One row tile (i) at a time, to bound the live registers.
-    uint8_t* tile = smem;
-    const int64_t gpr = p.N / G;
-    // (a compile-time row tile index keeps acc[i] in registers across the barriers)
-    auto row_tile = [&](auto I) __attribute__((always_inline)) {
-      constexpr int i = decltype(I)::value;
-      // Stage one: |C| maxima over G columns inside the wave.
-      float gmax[2][16];
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = row16_max(fabsf(acc[i][j][r]));
-          if constexpr (G >= 32) v = swap16_max(v);
-          gmax[j][r] = v;
-        }
-      if constexpr (G >= 64) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) gmax[0][r] = gmax[1][r] = fmaxf(gmax[0][r], gmax[1][r]);
-      }
-      // Stage two (G = 128): the two waves holding the same rows swap maxima.
-      if constexpr (G == 128) {
-        if (l32 == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            red[wn][wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3)] = gmax[0][r];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          gmax[0][r] = gmax[1][r] =
-              fmaxf(gmax[0][r], red[wn ^ 1][wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3)]);
-        __syncthreads();  // red is reused by the next row tile
-      }
-      // Quantize into the LDS code tile (128 x 128 bytes) and write the scales.
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float amax = gmax[j][r];
-          const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
-          const float rq = 448.0f / (amax * pre);
-          const float q = gq_scaled(acc[i][j][r] * pre, rq);
-          const uint32_t code =
-              amax > 0.0f ? ((uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFFu) : 0u;
           const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int col = wn * 64 + 32 * j + l32;
-          tile[row * kBN + col] = (uint8_t)code;
-          if (col % G == 0 && m0 + row < p.M)
-            p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
+          ct[row * kRowF + wn * 64 + 32 * j + l32] = acc[i][j][r];
         }
-    };
-    row_tile(std::integral_constant<int, 0>{});
-    row_tile(std::integral_constant<int, 1>{});
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = t + kBlockThreads * i, row = q >> 3, c = q & 7;
-      if (m0 + row < p.M) {
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN + 16 * c);
-        *reinterpret_cast<uint4*>(p.codes + (m0 + row) * p.N + n0 + 16 * c) = v;
+    const int chunk = t & 15, rsub = t >> 4;
+    const int64_t gpr = p.N / G;
+#pragma unroll 2
+    for (int q = 0; q < kBM / 16; ++q) {
+      const int row = 16 * q + rsub;
+      const int col = 8 * chunk;
+      const float4 v0 = *reinterpret_cast<const float4*>(ct + row * kRowF + col);
+      const float4 v1 = *reinterpret_cast<const float4*>(ct + row * kRowF + col + 4);
+      const bool ok = m0 + row < p.M;
+      if (p.c_f32 && ok) {
+        float* dst = p.c_f32 + (m0 + row) * p.N + n0 + col;
+        *reinterpret_cast<float4*>(dst) = v0;
+        *reinterpret_cast<float4*>(dst + 4) = v1;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                       fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+      // non-negative floats order like their bit patterns
+      const float amax = __uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mx)));
+      const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
+      const float rq = 448.0f / (amax * pre);
+      uint2 c = make_uint2(0u, 0u);
+      if (amax > 0.0f) {
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.x * pre, rq), gq_scaled(v0.y * pre, rq), 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.z * pre, rq), gq_scaled(v0.w * pre, rq), w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.x * pre, rq), gq_scaled(v1.y * pre, rq), 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.z * pre, rq), gq_scaled(v1.w * pre, rq), w1, true);
+        c = make_uint2((uint32_t)w0, (uint32_t)w1);
+      }
+      if (ok) {
+        *reinterpret_cast<uint2*>(p.codes + (m0 + row) * p.N + n0 + col) = c;
+        if (chunk % (G / 8) == 0) p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
       }
     }
   }

@@ -49,7 +49,10 @@ ACT_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_act.hip", "coat_common.h")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--path", choices=("adamw_step", "act_quant"), default="adamw_step")
+    ap.add_argument("--path", choices=("adamw_step", "act_quant", "gemm_group_quant"),
+                    default="adamw_step")
+    ap.add_argument("--gemm-shape", default="8192x11008x4096",
+                    help="M x N x K of the FP8 linear layer (gemm_group_quant)")
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20; 200 for act_quant)")
     ap.add_argument("--warmup", type=int, default=None,
@@ -67,10 +70,11 @@ def parse():
                     help="also run a plain device copy of known size (PMC calibration)")
     args = ap.parse_args()
     act = args.path == "act_quant"
+    gemm = args.path == "gemm_group_quant"
     if args.steps is None:
-        args.steps = 200 if act else 20
+        args.steps = 200 if act else (100 if gemm else 20)
     if args.warmup is None:
-        args.warmup = 20 if act else 5
+        args.warmup = 20 if act else (10 if gemm else 5)
     return args
 
 
@@ -324,6 +328,133 @@ def bench_act(args):
     print(json.dumps(rec), flush=True)
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix-core peak
+
+
+def cpu_baseline_gemm(a, b, sa, sb, G, min_seconds=10.0):
+    """The oracle's group-scaled linear layer timed on whole rows of the same
+    operands (rows are independent), split over host threads, repeated until
+    at least `min_seconds` of wall time."""
+    import numpy as np
+    import oracle
+
+    an, bn = a.cpu().numpy(), b.cpu().numpy()
+    M, K = an.shape
+    N = bn.shape[0]
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    rows_per_pass = 2 * threads
+    sel = [an[i:i + 2] for i in range(0, rows_per_pass * 1, 2)][:threads]
+
+    def run(x):
+        oracle.gemm_fp8_group_quant(x, bn, sa, sb, G)
+
+    passes = 0
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(run, sel))                      # untimed pass
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(run, sel))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    flops = passes * 2.0 * sum(x.shape[0] for x in sel) * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sum(x.shape[0] for x in sel)} of {M} rows x {N} x {K} (exact int64 "
+                      f"sums), {passes} passes after an untimed one, {dt:.2f} s wall"}
+
+
+def bench_gemm(args):
+    import torch
+    from adamw_coat_fp8_amd import coat, inputs
+
+    G = args.group_size
+    M, N, K = (int(v) for v in args.gemm_shape.lower().split("x"))
+    print(f"[bench] gemm_group_quant {M}x{N}x{K} G={G}", file=sys.stderr, flush=True)
+    torch.cuda.init()
+    a, b, sa, sb = inputs.fp8_operands(M, N, K, 0, "cuda", "llm")
+    codes = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((M, N // G), dtype=torch.float32, device="cuda")
+    c16 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * M * N * K
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        launch = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return wall * 1e3, sum(launch) / len(launch), launch[len(launch) // 2]
+
+    fused = lambda: coat.gemm_group_quant(a, b, sa, sb, codes, scales, group_size=G, stream=stream)
+    plain = lambda: coat.gemm_bf16(a, b, sa, sb, c16, stream=stream)
+    ms_wall, ms_launch, ms_med = timed(fused, args.steps, args.warmup)
+    print(f"[bench] fused: {ms_launch * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
+    _, ms_plain, _ = timed(plain, args.steps, args.warmup)
+    context = {"plain_bf16_epilogue_ms": round(ms_plain, 5),
+               "group_epilogue_overhead": round(ms_launch / ms_plain - 1.0, 4)}
+    # a library FP8 GEMM (hipBLASLt through torch) for context, if this build has one
+    try:
+        af = a.view(torch.float8_e4m3fn)
+        bf = b.view(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device="cuda")
+        lib_mm = lambda: torch._scaled_mm(af, bf.t(), scale_a=one, scale_b=one,
+                                          out_dtype=torch.bfloat16)
+        lib_mm()
+        _, ms_lib, _ = timed(lib_mm, max(10, args.steps // 4), 3)
+        context["library_fp8_gemm_bf16_ms"] = round(ms_lib, 5)
+        context["library_fp8_gemm_bf16_TFLOPs"] = round(flops / (ms_lib * 1e-3) / 1e12, 1)
+    except Exception as e:                      # noqa: BLE001 - context only
+        context["library_fp8_gemm_bf16"] = f"unavailable: {type(e).__name__}"
+    achieved = flops / (ms_launch * 1e-3) / 1e12
+    rec = {
+        "metric": "TFLOP/s per group-scaled FP8 linear layer (FP8 GEMM + fused 1xG group "
+                  "quantization of its output), 1 GPU",
+        "value": round(flops / (ms_wall * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"linear layer {M}x{N}x{K}: E4M3 activations (per-tensor) x E4M3 "
+                        f"weights (per-tensor), output 1x{G} group-quantized E4M3 + FP32 scales",
+            "group_size": G,
+            "launch_ms_median": round(ms_med, 5),
+            **context,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": f"gemm_fp8_kernel<{G}, group quant>",
+            "flops_per_launch": flops,
+            "avg_launch_ms": round(ms_launch, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_gemm(a, b, sa, sb, G)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -333,6 +464,8 @@ def main():
         sys.exit(2)
     if args.path == "act_quant":
         return bench_act(args)
+    if args.path == "gemm_group_quant":
+        return bench_gemm(args)
     import torch
     from adamw_coat_fp8_amd import coat, inputs
     from adamw_coat_fp8_amd.shard import FP8AdamWShard

@@ -28,6 +28,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "coat_common.h"
 
 using namespace coat;
@@ -38,9 +40,32 @@ constexpr int kBM = 128;
 constexpr int kBN = 128;
 constexpr int kBK = 128;
 constexpr int kPanelBytes = kBM * kBK;  // one A or B panel in LDS: 16 KB
-constexpr int kRowF = kBN + 4;          // padded FP32 row of the epilogue's C tile
-constexpr int kSmemBytes =
-    (4 * kPanelBytes > kBM * kRowF * 4) ? 4 * kPanelBytes : kBM * kRowF * 4;
+constexpr int kGroupM = 8;              // tile rows per group of the tile order
+
+// LDS: four distinct 16 KB arrays, the A and B panels of the two pipeline
+// stages.  Being distinct objects, the compiler can tell the direct-to-LDS
+// loads into one stage from the reads of the other, and does not wait for
+// the loads in flight before reading.  The epilogue reuses them as four
+// quarters (32 rows x 128 FP32 each) of the C tile.
+__shared__ __attribute__((aligned(16))) uint8_t lds_a0[kPanelBytes];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b0[kPanelBytes];
+__shared__ __attribute__((aligned(16))) uint8_t lds_a1[kPanelBytes];
+__shared__ __attribute__((aligned(16))) uint8_t lds_b1[kPanelBytes];
+
+template <int kQ>
+__device__ __forceinline__ uint8_t* lds_quarter() {
+  if constexpr (kQ == 0) return lds_a0;
+  else if constexpr (kQ == 1) return lds_b0;
+  else if constexpr (kQ == 2) return lds_a1;
+  else return lds_b1;
+}
+
+// Float offset of C[row % 32][col] in its quarter: 16-byte chunks XORed by
+// bit 2 of the row, so the two half-waves' rows (r and r + 4) fall 32 banks
+// apart; 8 consecutive columns (two chunks 2c, 2c + 1) stay adjacent.
+__device__ __forceinline__ int quarter_off(int row, int col) {
+  return (row & 31) * kBN + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (col & 3);
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -67,7 +92,13 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
 }
 
 // Byte offset of 16-byte chunk c of row `row` in a 128-byte-row LDS panel.
-__device__ __forceinline__ int panel_off(int row, int c) { return row * 128 + 16 * (c ^ (row & 7)); }
+// The LDS serves 16 lanes x 16 bytes (all 64 banks) per cycle.  An MFMA
+// operand read has 16 lanes on 16 consecutive rows at one logical chunk;
+// rows of opposite parity already sit in opposite halves of the banks, so
+// the chunk is XORed with (row / 2) % 8 to spread each parity class over the
+// 8 chunks of its half.
+__device__ __forceinline__ int chunk_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int panel_off(int row, int c) { return row * 128 + 16 * (c ^ chunk_swz(row)); }
 
 // Max over the kLanes neighbouring lanes of a group inside a 16-lane DPP row
 // (kLanes a power of two, groups aligned): quad swaps of 1 and 2 lanes, the
@@ -103,20 +134,26 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 template <int G, int kEpi>
 __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParams p) {
-  // A0 B0 A1 B1 panels in the main loop; the FP32 C tile in the epilogue
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  // Tile order: each XCD takes a contiguous run of tile indices, walked in
+  // groups of kGroupM tile rows, column by column inside a group, so the A
+  // panels of the group stay in the XCD's L2 and each B panel serves kGroupM
+  // tiles in a row.
   const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int64_t tm = bid / p.n_tiles, tn = bid - tm * p.n_tiles;
+  const int64_t m_tiles = (p.M + kBM - 1) / kBM;
+  const int64_t group = bid / (kGroupM * p.n_tiles), first_m = group * kGroupM;
+  const int64_t gm = m_tiles - first_m < kGroupM ? m_tiles - first_m : kGroupM;
+  const int64_t local = bid - group * kGroupM * p.n_tiles;
+  const int64_t tm = first_m + local % gm, tn = local / gm;
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
   const int64_t K = p.K;
 
   // Panel loads go straight from global memory into LDS: one wave-wide
   // 16-byte-per-lane load fills 1 KB, 8 rows of a panel, lane L landing at
   // byte 16 L.  So lane L carries row R0 + L/8 and the physical chunk L%8,
-  // which under the row swizzle holds logical chunk (L%8) ^ (L/8); the swizzle
-  // is applied on the global side.  Wave w fills rows 32 w .. 32 w + 31 of each
+  // which under the row swizzle holds logical chunk (L%8) ^ chunk_swz(row);
+  // the swizzle is applied on the global side.  Wave w fills rows 32 w .. 32 w + 31 of each
   // panel with 4 loads.  Rows of A past M are not loaded (their LDS bytes are
   // stale and only reach output rows that are never stored).
   const uint8_t* a_blk = p.a + m0 * K;
@@ -126,13 +163,14 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 32 * wave + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ (lane >> 3);
+    const int c = (lane & 7) ^ chunk_swz(row);
     goff[i] = (uint32_t)row * (uint32_t)K + 16u * (uint32_t)c;
     a_ok[i] = m0 + row < p.M;
   }
-  auto issue = [&](int64_t k0, int buf) __attribute__((always_inline)) {
-    uint8_t* As = smem + buf * 2 * kPanelBytes;
-    uint8_t* Bs = As + kPanelBytes;
+  auto issue = [&](int64_t k0, auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    uint8_t* As = lds_quarter<2 * st>();
+    uint8_t* Bs = lds_quarter<2 * st + 1>();
     const uint8_t* ak = a_blk + k0;
     const uint8_t* bk = b_blk + k0;
 #pragma unroll
@@ -153,14 +191,16 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = (int)(K / kBK);
-  if (nk > 0) issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const int half = lane >> 5, l32 = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) issue((int64_t)(kt + 1) * kBK, (kt + 1) & 1);
-    const uint8_t* As = smem + (kt & 1) * 2 * kPanelBytes;
-    const uint8_t* Bs = As + kPanelBytes;
+  // One K step on stage S: start the loads of step kt + 1 into the other
+  // stage, run the MFMAs on this one, then wait for this wave's loads and
+  // meet the other waves (their loads have landed, nobody reads stage S).
+  auto kstep = [&](int kt, auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    if (kt + 1 < nk) issue((int64_t)(kt + 1) * kBK, std::integral_constant<int, 1 - st>{});
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    const uint8_t* As = lds_quarter<2 * st>();
+    const uint8_t* Bs = lds_quarter<2 * st + 1>();
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       // lane supplies row (l32) and k bytes 64 kk + 32 half .. +31: chunks c0, c0 + 1
@@ -189,7 +229,16 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next panels have landed
     __syncthreads();
+  };
+  if (nk > 0) issue(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
   }
+  if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
 
   // Epilogue.  Value (i, j, r) of this lane is C[row][col] with
   //   row = wm*64 + 32 i + 8 (r/4) + 4 half + r%4,  col = wn*64 + 32 j + l32.
@@ -202,77 +251,110 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
       for (int r = 0; r < 16; ++r) acc[i][j][r] = scale_acc(acc[i][j][r], s);
 
   if constexpr (kEpi == kBF16) {
-    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // 128 x 128 BF16 = 32 KB
+    // BF16 tile: quarter q (rows 32 q .. 32 q + 31) in the first 8 KB of array q.
+    auto put = [&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      uint16_t* tile = reinterpret_cast<uint16_t*>(lds_quarter<q>());
+      if (wm == (q >> 1)) {
+        constexpr int i = q & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int col = wn * 64 + 32 * j + l32;
-          tile[row * kBN + col] = bf16_rne(acc[i][j][r]);
-        }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = t + kBlockThreads * i, row = q >> 4, c = q & 15;
-      if (m0 + row < p.M) {
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN + 8 * c);
-        *reinterpret_cast<uint4*>(p.c_bf16 + (m0 + row) * p.N + n0 + 8 * c) = v;
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+            tile[row * kBN + wn * 64 + 32 * j + l32] = bf16_rne(acc[i][j][r]);
+          }
       }
-    }
+    };
+    auto get = [&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      const uint16_t* tile = reinterpret_cast<const uint16_t*>(lds_quarter<q>());
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int qq = t + kBlockThreads * i, row = qq >> 4, c = qq & 15;
+        if (m0 + 32 * q + row < p.M) {
+          const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN + 8 * c);
+          *reinterpret_cast<uint4*>(p.c_bf16 + (m0 + 32 * q + row) * p.N + n0 + 8 * c) = v;
+        }
+      }
+    };
+    put(std::integral_constant<int, 0>{});
+    put(std::integral_constant<int, 1>{});
+    put(std::integral_constant<int, 2>{});
+    put(std::integral_constant<int, 3>{});
+    __syncthreads();
+    get(std::integral_constant<int, 0>{});
+    get(std::integral_constant<int, 1>{});
+    get(std::integral_constant<int, 2>{});
+    get(std::integral_constant<int, 3>{});
   } else {
-    // The scaled C tile goes to LDS as FP32 (rows padded to 132 floats), and
+    // The scaled C tile goes to LDS as FP32 (four 32-row quarters), and
     // the quantizer then walks it like the activation quantizer: a thread
     // takes 8 consecutive columns of a row per pass, so a group of G columns
     // sits on G/8 neighbouring lanes of a 16-lane DPP row.  Stage one of the
     // max is the thread's 8 values, stage two the DPP steps across the group's
     // lanes; the divisions (r and S) are once per 8 values.
-    float* ct = reinterpret_cast<float*>(smem);
+    auto put = [&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      float* ct = reinterpret_cast<float*>(lds_quarter<q>());
+      if (wm == (q >> 1)) {
+        constexpr int i = q & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * 64 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-          ct[row * kRowF + wn * 64 + 32 * j + l32] = acc[i][j][r];
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+            ct[quarter_off(row, wn * 64 + 32 * j + l32)] = acc[i][j][r];
+          }
+      }
+    };
+    put(std::integral_constant<int, 0>{});
+    put(std::integral_constant<int, 1>{});
+    put(std::integral_constant<int, 2>{});
+    put(std::integral_constant<int, 3>{});
     __syncthreads();
     const int chunk = t & 15, rsub = t >> 4;
     const int64_t gpr = p.N / G;
-#pragma unroll 2
-    for (int q = 0; q < kBM / 16; ++q) {
-      const int row = 16 * q + rsub;
-      const int col = 8 * chunk;
-      const float4 v0 = *reinterpret_cast<const float4*>(ct + row * kRowF + col);
-      const float4 v1 = *reinterpret_cast<const float4*>(ct + row * kRowF + col + 4);
-      const bool ok = m0 + row < p.M;
-      if (p.c_f32 && ok) {
-        float* dst = p.c_f32 + (m0 + row) * p.N + n0 + col;
-        *reinterpret_cast<float4*>(dst) = v0;
-        *reinterpret_cast<float4*>(dst + 4) = v1;
+    auto quantize = [&](auto Q) __attribute__((always_inline)) {
+      constexpr int qq = decltype(Q)::value;
+      const float* ct = reinterpret_cast<const float*>(lds_quarter<qq>());
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int lrow = 16 * h2 + rsub;      // row inside the quarter
+        const int row = 32 * qq + lrow;       // row inside the tile
+        const int col = 8 * chunk;
+        const float4 v0 = *reinterpret_cast<const float4*>(ct + quarter_off(lrow, col));
+        const float4 v1 = *reinterpret_cast<const float4*>(ct + quarter_off(lrow, col + 4));
+        const bool ok = m0 + row < p.M;
+        if (p.c_f32 && ok) {
+          float* dst = p.c_f32 + (m0 + row) * p.N + n0 + col;
+          *reinterpret_cast<float4*>(dst) = v0;
+          *reinterpret_cast<float4*>(dst + 4) = v1;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                         fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+        // non-negative floats order like their bit patterns
+        const float amax = __uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mx)));
+        const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
+        const float rq = 448.0f / (amax * pre);
+        uint2 c = make_uint2(0u, 0u);
+        if (amax > 0.0f) {
+          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.x * pre, rq), gq_scaled(v0.y * pre, rq), 0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.z * pre, rq), gq_scaled(v0.w * pre, rq), w0, true);
+          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.x * pre, rq), gq_scaled(v1.y * pre, rq), 0, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.z * pre, rq), gq_scaled(v1.w * pre, rq), w1, true);
+          c = make_uint2((uint32_t)w0, (uint32_t)w1);
+        }
+        if (ok) {
+          *reinterpret_cast<uint2*>(p.codes + (m0 + row) * p.N + n0 + col) = c;
+          if (chunk % (G / 8) == 0) p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
+        }
       }
-      float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                       fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-      // non-negative floats order like their bit patterns
-      const float amax = __uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mx)));
-      const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
-      const float rq = 448.0f / (amax * pre);
-      uint2 c = make_uint2(0u, 0u);
-      if (amax > 0.0f) {
-        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.x * pre, rq), gq_scaled(v0.y * pre, rq), 0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.z * pre, rq), gq_scaled(v0.w * pre, rq), w0, true);
-        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.x * pre, rq), gq_scaled(v1.y * pre, rq), 0, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.z * pre, rq), gq_scaled(v1.w * pre, rq), w1, true);
-        c = make_uint2((uint32_t)w0, (uint32_t)w1);
-      }
-      if (ok) {
-        *reinterpret_cast<uint2*>(p.codes + (m0 + row) * p.N + n0 + col) = c;
-        if (chunk % (G / 8) == 0) p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
-      }
-    }
+    };
+    quantize(std::integral_constant<int, 0>{});
+    quantize(std::integral_constant<int, 1>{});
+    quantize(std::integral_constant<int, 2>{});
+    quantize(std::integral_constant<int, 3>{});
   }
 }
 

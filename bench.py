@@ -40,10 +40,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_adamw_fp8_step_llama2_7b.txt")
 PMC_SUMMARY_ACT = os.path.join(ROOT, "profiles", "pmc_quantize_act_8192x11008.txt")
+PMC_SUMMARY_GEMM = os.path.join(ROOT, "profiles", "pmc_gemm_group_quant_8192x11008x4096.txt")
 _CSRC = os.path.join(ROOT, "adamw_coat_fp8_amd", "csrc")
 # the sources each profiled kernel is built from
 STEP_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_fp8.hip", "coat_common.h")]
 ACT_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_act.hip", "coat_common.h")]
+GEMM_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_gemm.hip", "coat_common.h")]
 
 
 def parse():
@@ -74,7 +76,7 @@ def parse():
     if args.steps is None:
         args.steps = 200 if act else (100 if gemm else 20)
     if args.warmup is None:
-        args.warmup = 20 if act else (10 if gemm else 5)
+        args.warmup = 20 if act else (30 if gemm else 5)
     return args
 
 
@@ -397,6 +399,8 @@ def bench_gemm(args):
 
     fused = lambda: coat.gemm_group_quant(a, b, sa, sb, codes, scales, group_size=G, stream=stream)
     plain = lambda: coat.gemm_bf16(a, b, sa, sb, c16, stream=stream)
+    for _ in range(args.warmup):          # both kernels warm (clocks, caches) before either is timed
+        plain()
     ms_wall, ms_launch, ms_med = timed(fused, args.steps, args.warmup)
     print(f"[bench] fused: {ms_launch * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
     _, ms_plain, _ = timed(plain, args.steps, args.warmup)
@@ -416,6 +420,13 @@ def bench_gemm(args):
     except Exception as e:                      # noqa: BLE001 - context only
         context["library_fp8_gemm_bf16"] = f"unavailable: {type(e).__name__}"
     achieved = flops / (ms_launch * 1e-3) / 1e12
+    if args.copy_probe:
+        copy_probe()
+    # minimum HBM bytes: read A and B once, write codes and scales once
+    min_bytes = M * K + N * K + M * N + 4 * M * (N // G)
+    traffic = (traffic_from_profile(min_bytes, PMC_SUMMARY_GEMM, GEMM_SOURCES)
+               if (M, N, K, G) == (8192, 11008, 4096, 128) else None)
+    context["min_hbm_bytes"] = min_bytes
     rec = {
         "metric": "TFLOP/s per group-scaled FP8 linear layer (FP8 GEMM + fused 1xG group "
                   "quantization of its output), 1 GPU",
@@ -443,7 +454,7 @@ def bench_gemm(args):
             "peak": MFMA_FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "kernel": f"gemm_fp8_kernel<{G}, group quant>",
             "flops_per_launch": flops,
             "avg_launch_ms": round(ms_launch, 5),

@@ -53,22 +53,6 @@ struct ActParams {
   int32_t vec_t;  // rows % 16 == 0: 16-byte stores into the transpose
 };
 
-// Max over the kLanes lanes of a group inside one 16-lane row: quad swaps of
-// 1 and 2 lanes, then the half-row mirror (joins two quads) and the row
-// mirror (joins two halves).
-template <int kLanes>
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
-  if constexpr (kLanes >= 2)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  if constexpr (kLanes >= 4)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  if constexpr (kLanes >= 8)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  if constexpr (kLanes >= 16)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  return v;
-}
-
 // Largest BF16 magnitude (as its 15 bits) among the 8 values of a chunk:
 // sign-cleared BF16 patterns order like the magnitudes they encode.
 __device__ __forceinline__ uint32_t bf16x8_max_mag(uint4 r) {
@@ -79,17 +63,9 @@ __device__ __forceinline__ uint32_t bf16x8_max_mag(uint4 r) {
   return max(max(a, b), max(c, d));
 }
 
-// x * r in FP32 (x already multiplied by the exact power-of-two prescale),
-// with -0 folded to +0 so that only values that round to zero in E4M3 keep a
-// negative sign.  Contraction is off: the product is rounded once, on its own.
-__device__ __forceinline__ float act_scaled(float x, float r) {
-#pragma clang fp contract(off)
-  return x * r + 0.0f;
-}
-
 __device__ __forceinline__ uint32_t act_pack4(uint32_t w0, uint32_t w1, float pre, float r) {
-  const float q0 = act_scaled(bf16_lo(w0) * pre, r), q1 = act_scaled(bf16_hi(w0) * pre, r);
-  const float q2 = act_scaled(bf16_lo(w1) * pre, r), q3 = act_scaled(bf16_hi(w1) * pre, r);
+  const float q0 = scaled_nz(bf16_lo(w0) * pre, r), q1 = scaled_nz(bf16_hi(w0) * pre, r);
+  const float q2 = scaled_nz(bf16_lo(w1) * pre, r), q3 = scaled_nz(bf16_hi(w1) * pre, r);
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, v, true);
   return (uint32_t)v;
@@ -115,15 +91,6 @@ __device__ __forceinline__ void store_stream8(void* p, uint2 v) {
 __device__ __forceinline__ void store_stream16(void* p, uint4 v) {
   const u32x4v w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4v*>(p));
-}
-
-// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).  This
-// maps launch index b to a tile index so that each XCD takes one contiguous
-// run of tiles (a bijection on [0, nb) for any nb).
-__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
-  const int64_t q = nb / 8, r = nb % 8;
-  const int64_t xcd = b % 8, local = b / 8;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
 // LDS tile: kActTileRows rows of 32 dwords.  The dword column is XOR-swizzled
@@ -163,7 +130,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_act_kernel(const ActPa
     const bool ok = col_ok && row < p.rows;
     // groups never straddle a validity boundary: a 16-lane row is one tile
     // row, and cols is a multiple of G
-    const uint32_t mag = row16_max_u32<kLanes>(bf16x8_max_mag(raw[q]));
+    const uint32_t mag = lanes_max_u32<kLanes>(bf16x8_max_mag(raw[q]));
     const float amax = __uint_as_float(mag << 16);
     // Below 2^-100, 448 / max would leave FP32's range: scale max and x by 2^64
     // (exact) so the rounded r and x*r are those of an unbounded exponent.

@@ -27,6 +27,42 @@ __attribute__((visibility("hidden"))) coat_status_t hip_fail(hipError_t e);
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Max over the kLanes neighbouring lanes of a group inside a 16-lane DPP row
+// (kLanes a power of two up to 16, groups aligned to kLanes): quad swaps of 1
+// and 2 lanes, the half-row mirror (joins two quads) and the row mirror
+// (joins two halves).  Every lane of the group ends with the group's max.
+template <int kLanes>
+__device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
+  static_assert(kLanes == 1 || kLanes == 2 || kLanes == 4 || kLanes == 8 || kLanes == 16,
+                "group inside one DPP row");
+  if constexpr (kLanes >= 2)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  if constexpr (kLanes >= 4)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  if constexpr (kLanes >= 8)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  if constexpr (kLanes >= 16)
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// x * r rounded once to FP32 (contraction off), with -0 folded to +0: the
+// FP32 product the per-group E4M3 quantizers round, so that only values that
+// round to zero in E4M3 keep a negative sign.
+__device__ __forceinline__ float scaled_nz(float x, float r) {
+#pragma clang fp contract(off)
+  return x * r + 0.0f;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+// Maps launch index b to a tile index so that each XCD takes one contiguous
+// run of tiles (a bijection on [0, nb) for any nb).
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
+  const int64_t q = nb / 8, r = nb % 8;
+  const int64_t xcd = b % 8, local = b / 8;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
 }  // namespace coat
 
 #endif  // COAT_COMMON_H

@@ -69,7 +69,6 @@ __device__ __forceinline__ int quarter_off(int row, int col) {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 
 enum Epilogue { kGroupQuant = 0, kBF16 = 1 };
 
@@ -85,11 +84,6 @@ struct GemmParams {
   float scale;       // a_scale * b_scale, rounded to FP32
 };
 
-__device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
-  const int64_t q = nb / 8, r = nb % 8;
-  const int64_t xcd = b % 8, local = b / 8;
-  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
 
 // Byte offset of 16-byte chunk c of row `row` in a 128-byte-row LDS panel.
 // The LDS serves 16 lanes x 16 bytes (all 64 banks) per cycle.  An MFMA
@@ -99,28 +93,6 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t b, int64_t nb) {
 // 8 chunks of its half.
 __device__ __forceinline__ int chunk_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int panel_off(int row, int c) { return row * 128 + 16 * (c ^ chunk_swz(row)); }
-
-// Max over the kLanes neighbouring lanes of a group inside a 16-lane DPP row
-// (kLanes a power of two, groups aligned): quad swaps of 1 and 2 lanes, the
-// half-row mirror (joins two quads), the row mirror (joins two halves).
-template <int kLanes>
-__device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
-  if constexpr (kLanes >= 2)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  if constexpr (kLanes >= 4)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-  if constexpr (kLanes >= 8)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
-  if constexpr (kLanes >= 16)
-    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
-  return v;
-}
-
-// x * r rounded once to FP32, -0 folded to +0 (see the activation quantizer).
-__device__ __forceinline__ float gq_scaled(float x, float r) {
-#pragma clang fp contract(off)
-  return x * r + 0.0f;
-}
 
 __device__ __forceinline__ float scale_acc(float acc, float s) {
 #pragma clang fp contract(off)
@@ -339,10 +311,10 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
         const float rq = 448.0f / (amax * pre);
         uint2 c = make_uint2(0u, 0u);
         if (amax > 0.0f) {
-          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.x * pre, rq), gq_scaled(v0.y * pre, rq), 0, false);
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v0.z * pre, rq), gq_scaled(v0.w * pre, rq), w0, true);
-          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.x * pre, rq), gq_scaled(v1.y * pre, rq), 0, false);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(gq_scaled(v1.z * pre, rq), gq_scaled(v1.w * pre, rq), w1, true);
+          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.x * pre, rq), scaled_nz(v0.y * pre, rq), 0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.z * pre, rq), scaled_nz(v0.w * pre, rq), w0, true);
+          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.x * pre, rq), scaled_nz(v1.y * pre, rq), 0, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.z * pre, rq), scaled_nz(v1.w * pre, rq), w1, true);
           c = make_uint2((uint32_t)w0, (uint32_t)w1);
         }
         if (ok) {

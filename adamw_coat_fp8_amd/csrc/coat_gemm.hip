@@ -10,7 +10,8 @@
 //        核心公式 "FP8量化" for the per-group quantizer.
 //   [OCP] OFP8 specification, E4M3.
 //
-// Execution model.  C = s * A B^T with A (M x K) and B (N x K) E4M3 codes,
+// Execution model (128 x 128 tiles; a 256 x 256 variant further down is used
+// when N is a multiple of 256).  C = s * A B^T with A (M x K) and B (N x K) E4M3 codes,
 // row-major, s = a_scale * b_scale.  A 256-thread block computes a 128 x 128
 // tile of C; its four waves each own 64 x 64 as 2 x 2 tiles of the 32x32x64
 // FP8 MFMA, accumulating in FP32.  K advances 128 at a time through a double
@@ -330,18 +331,283 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
   }
 }
 
-template <int G>
-const void* gq_fn() {
-  return reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kGroupQuant>);
+// ------------------------------------------------------ 256 x 256 tiles
+//
+// The same GEMM with 256 x 256 block tiles: 512 threads, eight waves (2 x 4)
+// of 128 x 64 each (4 x 2 MFMA tiles).  Per unit of output it moves half the
+// panel traffic of the 128 x 128 kernel; the LDS holds 2 stages of 32 KB A
+// and B panels (128 KB), so one block runs per CU.  The epilogue stages the
+// FP32 tile through the same four arrays in two passes of 128 rows (every
+// wave writes two of its four row tiles per pass).  Used when N is a multiple
+// of 256.
+
+constexpr int kBM256 = 256;
+constexpr int kBN256 = 256;
+constexpr int kThreads256 = 512;
+constexpr int kPanel256 = kBM256 * kBK;  // 32 KB
+constexpr int kGroupM256 = 4;            // tile rows per group of the tile order
+
+__shared__ __attribute__((aligned(16))) uint8_t lds256_a0[kPanel256];
+__shared__ __attribute__((aligned(16))) uint8_t lds256_b0[kPanel256];
+__shared__ __attribute__((aligned(16))) uint8_t lds256_a1[kPanel256];
+__shared__ __attribute__((aligned(16))) uint8_t lds256_b1[kPanel256];
+
+template <int kQ>
+__device__ __forceinline__ uint8_t* lds256_part() {
+  if constexpr (kQ == 0) return lds256_a0;
+  else if constexpr (kQ == 1) return lds256_b0;
+  else if constexpr (kQ == 2) return lds256_a1;
+  else return lds256_b1;
 }
 
-const void* gemm_kernel_for(int32_t g, int epi) {
-  if (epi == kBF16) return reinterpret_cast<const void*>(&gemm_fp8_kernel<128, kBF16>);
+// Float offset of C[row % 32][col] in a 32-row x 256-column FP32 part, with
+// the same chunk XOR as the 128-column quarters.
+__device__ __forceinline__ int part256_off(int row, int col) {
+  return (row & 31) * kBN256 + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (col & 3);
+}
+
+template <int G, int kEpi>
+__global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmParams p) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave & 1, wn = wave >> 1;   // 2 x 4 waves of 128 x 64
+  // Tile order: each XCD takes a contiguous run of tile indices, walked in
+  // groups of kGroupM256 tile rows, column by column inside a group, so the A
+  // panels of the group stay in the XCD's L2 and each B panel serves kGroupM256
+  // tiles in a row.
+  const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t m_tiles = (p.M + kBM256 - 1) / kBM256;
+  const int64_t group = bid / (kGroupM256 * p.n_tiles), first_m = group * kGroupM256;
+  const int64_t gm = m_tiles - first_m < kGroupM256 ? m_tiles - first_m : kGroupM256;
+  const int64_t local = bid - group * kGroupM256 * p.n_tiles;
+  const int64_t tm = first_m + local % gm, tn = local / gm;
+  const int64_t m0 = tm * kBM256, n0 = tn * kBN256;
+  const int64_t K = p.K;
+
+  // Panel loads go straight from global memory into LDS: one wave-wide
+  // 16-byte-per-lane load fills 1 KB, 8 rows of a panel, lane L landing at
+  // byte 16 L.  So lane L carries row R0 + L/8 and the physical chunk L%8,
+  // which under the row swizzle holds logical chunk (L%8) ^ chunk_swz(row);
+  // the swizzle is applied on the global side.  Wave w fills rows 32 w .. 32 w + 31 of each
+  // panel with 4 loads.  Rows of A past M are not loaded (their LDS bytes are
+  // stale and only reach output rows that are never stored).
+  const uint8_t* a_blk = p.a + m0 * K;
+  const uint8_t* b_blk = p.b + n0 * K;
+  uint32_t goff[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ chunk_swz(row);
+    goff[i] = (uint32_t)row * (uint32_t)K + 16u * (uint32_t)c;
+    a_ok[i] = m0 + row < p.M;
+  }
+  auto issue = [&](int64_t k0, auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    uint8_t* As = lds256_part<2 * st>();
+    uint8_t* Bs = lds256_part<2 * st + 1>();
+    const uint8_t* ak = a_blk + k0;
+    const uint8_t* bk = b_blk + k0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint8_t* dst_a = As + 1024 * (4 * wave + i);
+      uint8_t* dst_b = Bs + 1024 * (4 * wave + i);
+      if (a_ok[i]) __builtin_amdgcn_global_load_lds(ak + goff[i], dst_a, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bk + goff[i], dst_b, 16, 0, 0);
+    }
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (int)(K / kBK);
+  const int half = lane >> 5, l32 = lane & 31;
+  // One K step on stage S: start the loads of step kt + 1 into the other
+  // stage, run the MFMAs on this one, then wait for this wave's loads and
+  // meet the other waves (their loads have landed, nobody reads stage S).
+  auto kstep = [&](int kt, auto S) __attribute__((always_inline)) {
+    constexpr int st = decltype(S)::value;
+    if (kt + 1 < nk) issue((int64_t)(kt + 1) * kBK, std::integral_constant<int, 1 - st>{});
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    const uint8_t* As = lds256_part<2 * st>();
+    const uint8_t* Bs = lds256_part<2 * st + 1>();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // lane supplies row (l32) and k bytes 64 kk + 32 half .. +31: chunks c0, c0 + 1
+      const int c0 = 4 * kk + 2 * half;
+      v8i fa[4], fb[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + 32 * i + l32;
+        const uint4 lo = *reinterpret_cast<const uint4*>(As + panel_off(row, c0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(As + panel_off(row, c0 + 1));
+        fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wn * 64 + 32 * j + l32;
+        const uint4 lo = *reinterpret_cast<const uint4*>(Bs + panel_off(row, c0));
+        const uint4 hi = *reinterpret_cast<const uint4*>(Bs + panel_off(row, c0 + 1));
+        fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0,
+                                                                      0, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next panels have landed
+    __syncthreads();
+  };
+  if (nk > 0) issue(0, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
+
+  // Epilogue.  Value (i, j, r) of this lane is C[row][col] with
+  //   row = wm*64 + 32 i + 8 (r/4) + 4 half + r%4,  col = wn*64 + 32 j + l32.
+  const float s = p.scale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = scale_acc(acc[i][j][r], s);
+
+  if constexpr (kEpi == kBF16) {
+    // BF16 tile: array q holds rows 64 q .. 64 q + 63 (64 x 256 x 2 bytes).
+    auto put = [&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      uint16_t* tile = reinterpret_cast<uint16_t*>(lds256_part<q>());
+      if (wm == (q >> 1)) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * (q & 1) + ii;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = 32 * ii + 8 * (r >> 2) + 4 * half + (r & 3);
+              tile[row * kBN256 + wn * 64 + 32 * j + l32] = bf16_rne(acc[i][j][r]);
+            }
+        }
+      }
+    };
+    auto get = [&](auto Q) __attribute__((always_inline)) {
+      constexpr int q = decltype(Q)::value;
+      const uint16_t* tile = reinterpret_cast<const uint16_t*>(lds256_part<q>());
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qq = t + kThreads256 * i, row = qq >> 5, c = qq & 31;
+        if (m0 + 64 * q + row < p.M) {
+          const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN256 + 8 * c);
+          *reinterpret_cast<uint4*>(p.c_bf16 + (m0 + 64 * q + row) * p.N + n0 + 8 * c) = v;
+        }
+      }
+    };
+    put(std::integral_constant<int, 0>{});
+    put(std::integral_constant<int, 1>{});
+    put(std::integral_constant<int, 2>{});
+    put(std::integral_constant<int, 3>{});
+    __syncthreads();
+    get(std::integral_constant<int, 0>{});
+    get(std::integral_constant<int, 1>{});
+    get(std::integral_constant<int, 2>{});
+    get(std::integral_constant<int, 3>{});
+  } else {
+    const int chunk = t & 31, rsub = t >> 5;
+    const int64_t gpr = p.N / G;
+    auto pass = [&](auto P) __attribute__((always_inline)) {
+      constexpr int ps = decltype(P)::value;
+      // Every wave writes its row tiles i = 2 ps, 2 ps + 1: array k holds the
+      // 32 rows 128 (k / 2) + 32 ((k % 2) + 2 ps) .. + 31 of the tile.
+      auto put = [&](auto Q) __attribute__((always_inline)) {
+        constexpr int ii = decltype(Q)::value;           // 0, 1
+        constexpr int i = 2 * ps + ii;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+            const int off = part256_off(row, wn * 64 + 32 * j + l32);
+            if (wm == 0) reinterpret_cast<float*>(lds256_part<ii>())[off] = acc[i][j][r];
+            else reinterpret_cast<float*>(lds256_part<2 + ii>())[off] = acc[i][j][r];
+          }
+      };
+      put(std::integral_constant<int, 0>{});
+      put(std::integral_constant<int, 1>{});
+      __syncthreads();
+      auto quantize = [&](auto Q) __attribute__((always_inline)) {
+        constexpr int qq = decltype(Q)::value;
+        const float* ct = reinterpret_cast<const float*>(lds256_part<qq>());
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int lrow = 16 * h2 + rsub;              // row inside the array
+          const int row = 128 * (qq >> 1) + 32 * ((qq & 1) + 2 * ps) + lrow;  // row inside the tile
+          const int col = 8 * chunk;
+          const float4 v0 = *reinterpret_cast<const float4*>(ct + part256_off(lrow, col));
+          const float4 v1 = *reinterpret_cast<const float4*>(ct + part256_off(lrow, col + 4));
+          const bool ok = m0 + row < p.M;
+          if (p.c_f32 && ok) {
+            float* dst = p.c_f32 + (m0 + row) * p.N + n0 + col;
+            *reinterpret_cast<float4*>(dst) = v0;
+            *reinterpret_cast<float4*>(dst + 4) = v1;
+          }
+          float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                           fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+          const float amax = __uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mx)));
+          const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
+          const float rq = 448.0f / (amax * pre);
+          uint2 c = make_uint2(0u, 0u);
+          if (amax > 0.0f) {
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.x * pre, rq), scaled_nz(v0.y * pre, rq), 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.z * pre, rq), scaled_nz(v0.w * pre, rq), w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.x * pre, rq), scaled_nz(v1.y * pre, rq), 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.z * pre, rq), scaled_nz(v1.w * pre, rq), w1, true);
+            c = make_uint2((uint32_t)w0, (uint32_t)w1);
+          }
+          if (ok) {
+            *reinterpret_cast<uint2*>(p.codes + (m0 + row) * p.N + n0 + col) = c;
+            if (chunk % (G / 8) == 0) p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
+          }
+        }
+      };
+      quantize(std::integral_constant<int, 0>{});
+      quantize(std::integral_constant<int, 1>{});
+      quantize(std::integral_constant<int, 2>{});
+      quantize(std::integral_constant<int, 3>{});
+    };
+    pass(std::integral_constant<int, 0>{});
+    __syncthreads();   // the arrays are rewritten by the second pass
+    pass(std::integral_constant<int, 1>{});
+  }
+}
+
+template <int G>
+const void* gq_fn(bool big) {
+  return big ? reinterpret_cast<const void*>(&gemm_fp8_kernel_256<G, kGroupQuant>)
+             : reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kGroupQuant>);
+}
+
+const void* gemm_kernel_for(int32_t g, int epi, bool big) {
+  if (epi == kBF16)
+    return big ? reinterpret_cast<const void*>(&gemm_fp8_kernel_256<128, kBF16>)
+               : reinterpret_cast<const void*>(&gemm_fp8_kernel<128, kBF16>);
   switch (g) {
-    case 16: return gq_fn<16>();
-    case 32: return gq_fn<32>();
-    case 64: return gq_fn<64>();
-    default: return gq_fn<128>();
+    case 16: return gq_fn<16>(big);
+    case 32: return gq_fn<32>(big);
+    case 64: return gq_fn<64>(big);
+    default: return gq_fn<128>(big);
   }
 }
 
@@ -358,12 +624,15 @@ coat_status_t check_gemm_shape(const uint8_t* a, const uint8_t* b, float a_scale
   return COAT_OK;
 }
 
+// 256 x 256 tiles when N allows them (N % 256 == 0), else 128 x 128.
 hipError_t launch_gemm(GemmParams& p, int32_t group_size, int epi, hipStream_t stream) {
-  p.n_tiles = p.N / kBN;
-  const int64_t blocks = (p.M + kBM - 1) / kBM * p.n_tiles;
+  const bool big = p.N % kBN256 == 0;
+  const int64_t bm = big ? kBM256 : kBM, bn = big ? kBN256 : kBN;
+  p.n_tiles = p.N / bn;
+  const int64_t blocks = (p.M + bm - 1) / bm * p.n_tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(gemm_kernel_for(group_size, epi), dim3((unsigned)blocks),
-                         dim3(kBlockThreads), args, 0, stream);
+  return hipLaunchKernel(gemm_kernel_for(group_size, epi, big), dim3((unsigned)blocks),
+                         dim3(big ? kThreads256 : kBlockThreads), args, 0, stream);
 }
 
 }  // namespace

@@ -404,8 +404,18 @@ def bench_gemm(args):
     ms_wall, ms_launch, ms_med = timed(fused, args.steps, args.warmup)
     print(f"[bench] fused: {ms_launch * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
     _, ms_plain, _ = timed(plain, args.steps, args.warmup)
+    # the unfused alternative: the plain GEMM, then the activation quantizer on its BF16 output
+    codes2 = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    scales2 = torch.empty((M, N // G), dtype=torch.float32, device="cuda")
+    c16b = c16.view(torch.bfloat16)
+    unfused = lambda: (plain(), coat.quantize_act(c16b, codes2, scales2, None, group_size=G,
+                                                  stream=stream))
+    _, ms_unfused, _ = timed(unfused, args.steps, args.warmup)
     context = {"plain_bf16_epilogue_ms": round(ms_plain, 5),
-               "group_epilogue_overhead": round(ms_launch / ms_plain - 1.0, 4)}
+               "group_epilogue_overhead": round(ms_launch / ms_plain - 1.0, 4),
+               "unfused_bf16_gemm_then_quantizer_ms": round(ms_unfused, 5),
+               "fused_saving_vs_unfused": round(1.0 - ms_launch / ms_unfused, 4),
+               "tile": "256x256" if N % 256 == 0 else "128x128"}
     # a library FP8 GEMM (hipBLASLt through torch) for context, if this build has one
     try:
         af = a.view(torch.float8_e4m3fn)

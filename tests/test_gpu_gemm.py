@@ -62,8 +62,9 @@ def _assert_bit_exact(tag, gpu, ref):
         assert np.array_equal(g32.view(np.uint32), r32.view(np.uint32)), f"{tag}: C differs"
 
 
+# N % 256 == 0 takes the 256 x 256 tile kernel, N % 256 == 128 the 128 x 128 one
 EXACT_SHAPES = [(1, 128, 128), (100, 256, 256), (128, 128, 512), (257, 384, 128),
-                (64, 1024, 1024), (5, 128, 0)]
+                (64, 1024, 1024), (5, 128, 0), (300, 512, 384), (17, 768, 128), (5, 256, 0)]
 
 
 @pytest.mark.parametrize("G", [16, 32, 64, 128])
@@ -121,7 +122,8 @@ def _interval_check(tag, a, b, sa, sb, G, gpu, rows=None):
 
 
 @pytest.mark.parametrize("G", [16, 32, 64, 128])
-@pytest.mark.parametrize("shape", [(96, 256, 512), (200, 384, 1024), (64, 128, 4096)])
+@pytest.mark.parametrize("shape", [(96, 256, 512), (200, 384, 1024), (64, 128, 4096),
+                                   (300, 512, 512)])
 def test_llm_inputs_within_bound(G, shape):
     M, N, K = shape
     a, b, sa, sb = inputs.fp8_operands(M, N, K, 2, DEV, "llm")
@@ -205,7 +207,8 @@ def test_full_size_sampled_rows():
     _interval_check("full llm", a, b, sa, sb, G, (gc[sel], gs[sel], None), rows=sel)
 
 
-@pytest.mark.parametrize("shape", [(1, 128, 128), (257, 384, 256), (128, 1024, 1024)])
+@pytest.mark.parametrize("shape", [(1, 128, 128), (257, 384, 256), (128, 1024, 1024),
+                                   (300, 512, 256)])
 def test_bf16_epilogue(shape):
     coat = lib()
     M, N, K = shape

@@ -1,7 +1,9 @@
 """ctypes binding of libcoat_fp8.so (declared in include/coat_fp8.h).
 
 Argument marshalling only: every step of the optimizer runs in the library's
-HIP kernels.  torch tensors are accepted for convenience (their device pointers
+HIP kernels.  Marshalling includes what the C ABI cannot see through raw
+pointers: each buffer's dtype, contiguity, size and device are checked
+before the call (ValueError).  torch tensors are accepted for convenience (their device pointers
 and torch's current HIP stream are passed through); the library never sees a
 torch type.  Importing this module loads the library and fails loudly if it is
 missing: there is no fallback implementation.
@@ -114,6 +116,33 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+# dtypes accepted for each kind of buffer (bit-pattern views are fine)
+CODE_DTYPES = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+BF16_DTYPES = (torch.bfloat16, torch.int16)
+F32_DTYPES = (torch.float32,)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, min_numel: int):
+    """Marshalling checks the C ABI cannot make: the kernels read and write
+    through raw device pointers, so a buffer of the wrong type, layout, size
+    or device would be accessed out of bounds.  Raises ValueError."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {min_numel}")
+
+
+def _on_device(**tensors):
+    """Every given buffer is HIP device memory (after the type and size checks)."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a CUDA (HIP device) tensor, not {t.device}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -143,6 +172,15 @@ class QuantState:
     def as_c(self) -> FP8State:
         return FP8State(_ptr(self.codes), _ptr(self.scale), _ptr(self.k))
 
+    def check(self, n: int, group_size: int, name: str):
+        _need(self.codes, f"{name}.codes", CODE_DTYPES, n)
+        _need(self.scale, f"{name}.scale", F32_DTYPES, num_groups(n, group_size))
+        _need(self.k, f"{name}.k", F32_DTYPES, num_groups(n, group_size))
+
+    def check_device(self, name: str):
+        _on_device(**{f"{name}.codes": self.codes, f"{name}.scale": self.scale,
+                      f"{name}.k": self.k})
+
 
 @dataclass
 class ParamSlot:
@@ -156,6 +194,16 @@ class ParamSlot:
         return AdamWTensor(_ptr(self.w), _ptr(self.grad), self.m.as_c(),
                            self.v.as_c(), self.w.numel())
 
+    def check(self, group_size: int, name: str = "slot"):
+        n = self.w.numel()
+        _need(self.w, f"{name}.w", F32_DTYPES, n)
+        _need(self.grad, f"{name}.grad", BF16_DTYPES, n)
+        self.m.check(n, group_size, f"{name}.m")
+        self.v.check(n, group_size, f"{name}.v")
+        _on_device(**{f"{name}.w": self.w, f"{name}.grad": self.grad})
+        self.m.check_device(f"{name}.m")
+        self.v.check_device(f"{name}.v")
+
 
 class TensorList:
     """Marshalled descriptor array for coat_adamw_fp8_step, built once and
@@ -165,6 +213,13 @@ class TensorList:
         self.slots = list(slots)
         self.array = (AdamWTensor * max(1, len(self.slots)))(
             *[s.as_c() for s in self.slots])
+        self._checked = set()   # group sizes the slots have been checked for
+
+    def check(self, group_size: int):
+        if group_size not in self._checked:
+            for i, slot in enumerate(self.slots):
+                slot.check(group_size, f"tensors[{i}]")
+            self._checked.add(group_size)
 
     def __len__(self):
         return len(self.slots)
@@ -175,6 +230,7 @@ def adamw_fp8_step(tensors, *, lr: float, beta1: float, beta2: float, eps: float
     """One fused FP8 AdamW step over `tensors` (a TensorList or a sequence of
     ParamSlot).  Enqueued on `stream` (torch's current stream by default)."""
     tl = tensors if isinstance(tensors, TensorList) else TensorList(tensors)
+    tl.check(group_size)
     hp = AdamWHParams(lr, beta1, beta2, eps, weight_decay, step, group_size)
     _check(lib.coat_adamw_fp8_step(ctypes.addressof(tl.array), len(tl),
                                    ctypes.byref(hp), _stream(stream)))
@@ -189,22 +245,36 @@ def adamw_fp8_step_raw(array_ptr: Optional[int], num_tensors: int, hp: AdamWHPar
 
 
 def expand_quantize(x: torch.Tensor, out: QuantState, group_size: int = 128, stream=None):
+    _need(x, "x", F32_DTYPES, 0)
+    out.check(x.numel(), group_size, "out")
+    _on_device(x=x)
+    out.check_device("out")
     _check(lib.coat_fp8_expand_quantize(_ptr(x), x.numel(), group_size, out.as_c(),
                                         _stream(stream)))
 
 
 def dequantize_expand(state: QuantState, out: torch.Tensor, group_size: int = 128,
                       stream=None):
+    state.check(state.codes.numel(), group_size, "state")
+    _need(out, "out", F32_DTYPES, state.codes.numel())
+    state.check_device("state")
+    _on_device(out=out)
     _check(lib.coat_fp8_dequantize_expand(
         _ptr(state.codes), _ptr(state.scale), _ptr(state.k), state.codes.numel(),
         group_size, _ptr(out), _stream(stream)))
 
 
 def e4m3_encode(x: torch.Tensor, codes: torch.Tensor, stream=None):
+    _need(x, "x", F32_DTYPES, 0)
+    _need(codes, "codes", CODE_DTYPES, x.numel())
+    _on_device(x=x, codes=codes)
     _check(lib.coat_e4m3_encode(_ptr(x), x.numel(), _ptr(codes), _stream(stream)))
 
 
 def e4m3_decode(codes: torch.Tensor, x: torch.Tensor, stream=None):
+    _need(codes, "codes", CODE_DTYPES, 0)
+    _need(x, "x", F32_DTYPES, codes.numel())
+    _on_device(codes=codes, x=x)
     _check(lib.coat_e4m3_decode(_ptr(codes), codes.numel(), _ptr(x), _stream(stream)))
 
 
@@ -217,6 +287,12 @@ def quantize_act(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     if x.dim() != 2:
         raise ValueError("quantize_act expects a 2-D (rows, cols) tensor")
     rows, cols = x.shape
+    _need(x, "x", BF16_DTYPES, 0)
+    _need(codes, "codes", CODE_DTYPES, rows * cols)
+    _need(scales, "scales", F32_DTYPES, rows * (cols // max(group_size, 1)))
+    if codes_t is not None:
+        _need(codes_t, "codes_t", CODE_DTYPES, rows * cols)
+    _on_device(x=x, codes=codes, scales=scales, codes_t=codes_t)
     _check(lib.coat_fp8_quantize_act(_ptr(x), rows, cols, group_size, _ptr(codes),
                                      _ptr(scales), _ptr(codes_t), _stream(stream)))
 
@@ -231,6 +307,13 @@ def gemm_group_quant(a: torch.Tensor, b: torch.Tensor, a_scale: float, b_scale: 
     N = b.shape[0]
     if b.shape[1] != K:
         raise ValueError("a and b disagree on K")
+    _need(a, "a", CODE_DTYPES, 0)
+    _need(b, "b", CODE_DTYPES, 0)
+    _need(codes, "codes", CODE_DTYPES, M * N)
+    _need(scales, "scales", F32_DTYPES, M * (N // max(group_size, 1)))
+    if c_f32 is not None:
+        _need(c_f32, "c_f32", F32_DTYPES, M * N)
+    _on_device(a=a, b=b, codes=codes, scales=scales, c_f32=c_f32)
     _check(lib.coat_fp8_gemm_group_quant(_ptr(a), _ptr(b), a_scale, b_scale, M, N, K,
                                          group_size, _ptr(codes), _ptr(scales), _ptr(c_f32),
                                          _stream(stream)))
@@ -243,5 +326,9 @@ def gemm_bf16(a: torch.Tensor, b: torch.Tensor, a_scale: float, b_scale: float,
     N = b.shape[0]
     if b.shape[1] != K:
         raise ValueError("a and b disagree on K")
+    _need(a, "a", CODE_DTYPES, 0)
+    _need(b, "b", CODE_DTYPES, 0)
+    _need(c_bf16, "c_bf16", BF16_DTYPES, M * N)
+    _on_device(a=a, b=b, c_bf16=c_bf16)
     _check(lib.coat_fp8_gemm_bf16(_ptr(a), _ptr(b), a_scale, b_scale, M, N, K, _ptr(c_bf16),
                                   _stream(stream)))

@@ -135,6 +135,54 @@ def test_resume_through_host_equals_straight_run():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+def test_graph_capture_replays_match_eager():
+    """One step captured in a HIP graph (the step count is a launch argument,
+    so the graph replays step t = 5) and replayed three times, with eager work
+    and a synchronization between replays: after every replay the state equals
+    three eager calls of the same step, bit for bit."""
+    coat = lib()
+    n, G, t = 300_000 + 11, 128, 5
+
+    def fresh():
+        w = inputs.weights(n, 0, DEV)
+        m = coat.QuantState.zeros(n, G, DEV)
+        v = coat.QuantState.zeros(n, G, DEV)
+        for s in (1, 2):                                  # warm, nonzero state
+            coat.adamw_fp8_step([coat.ParamSlot(w, inputs.gradient(n, 1e-3, s, 0, DEV), m, v)],
+                                **HP, step=s, group_size=G)
+        return w, inputs.gradient(n, 1e-3, t, 0, DEV), m, v
+
+    def state(w, m, v):
+        return [x.clone() for x in (w, m.codes, m.scale, m.k, v.codes, v.scale, v.k)]
+
+    we, ge, me, ve = fresh()
+    wg, gg, mg, vg = fresh()
+    torch.cuda.synchronize()
+    eager_list = coat.TensorList([coat.ParamSlot(we, ge, me, ve)])
+    graph_list = coat.TensorList([coat.ParamSlot(wg, gg, mg, vg)])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                          # warm the capture stream
+        graph_list.check(G)
+    torch.cuda.current_stream().wait_stream(side)
+    before = state(wg, mg, vg)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        coat.adamw_fp8_step(graph_list, **HP, step=t, group_size=G)
+    torch.cuda.synchronize()
+    # capturing does not execute the step
+    assert all(torch.equal(a, b) for a, b in zip(before, state(wg, mg, vg)))
+    for replay in range(3):
+        graph.replay()
+        coat.adamw_fp8_step(eager_list, **HP, step=t, group_size=G)
+        scratch = torch.randn(1 << 16, device=DEV).sum()      # eager work between replays
+        torch.cuda.synchronize()
+        a, b = state(we, me, ve), state(wg, mg, vg)
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), f"replay {replay}"
+        del scratch
+
+
 def test_free_running_drift_report():
     """GPU and oracle each run 10 steps on their own from zero state.  Not a
     parity gate: each side's rounding feeds its next step, and the first

@@ -11,17 +11,27 @@
 //   [OCP] OFP8 specification, E4M3.
 //
 // Execution model (128 x 128 tiles; a 256 x 256 variant further down is used
-// when N is a multiple of 256).  C = s * A B^T with A (M x K) and B (N x K) E4M3 codes,
-// row-major, s = a_scale * b_scale.  A 256-thread block computes a 128 x 128
-// tile of C; its four waves each own 64 x 64 as 2 x 2 tiles of the 32x32x64
-// FP8 MFMA, accumulating in FP32.  K advances 128 at a time through a double
-// buffered LDS copy of the A and B panels, loaded straight from global memory
-// into LDS (16-byte chunks XOR-swizzled by row, so the MFMA operand reads are
-// free of bank conflicts) while the MFMAs of the previous panels run.  In the 32x32 MFMA result a row's 32 columns lie across
-// the 32 lanes of a half wave; the epilogue therefore stages the scaled FP32
-// tile through LDS and re-reads it row-contiguously, 8 columns per lane, so
-// that the group max is stage one over a lane's 8 values and stage two over
-// the group's G/8 lanes (DPP), with the two divisions per 8 values.
+// when N is a multiple of 256).  C = s * A B^T with A (M x K) and B (N x K)
+// E4M3 codes, row-major, s = a_scale * b_scale.  A 256-thread block computes
+// a 128 x 128 tile of C; its four waves each own 64 x 64 as 2 x 2 tiles of
+// the 32x32x64 FP8 MFMA, accumulating in FP32.  K advances 128 at a time
+// through a double buffered LDS copy of the A and B panels, loaded straight
+// from global memory into LDS (16-byte chunks XOR-swizzled by row, so the
+// MFMA operand reads are free of bank conflicts) while the MFMAs of the
+// previous panels run.  In the 32x32 MFMA result a row's 32 columns lie
+// across the 32 lanes of a half wave; the epilogue therefore stages the FP32
+// accumulator tile through LDS and re-reads it row-contiguously, 8 columns
+// per lane, so that the group max is stage one over a lane's 8 values and
+// stage two over the group's G/8 lanes (DPP).
+//
+// Quantization (both kernels).  With c the FP32 accumulator, the group
+// maximum of |c s| is fl(max |c| * |s|) exactly (rounding is monotone), the
+// stored scale is that maximum / 448, and each code is RNE(c * m) with the
+// per-group multiplier m = fl(s * fl(448 / max)): one rounding of c per
+// element instead of the two of fl(fl(c s) * 448 / max).  Both agree
+// bit for bit when s is a power of two; otherwise they differ by at most one
+// FP32 rounding of the value rounded to E4M3.  Groups whose maximum lies
+// below 2^-100 or past FP32's range take the two-rounding form.
 
 #include <hip/hip_runtime.h>
 
@@ -216,14 +226,14 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
   // Epilogue.  Value (i, j, r) of this lane is C[row][col] with
   //   row = wm*64 + 32 i + 8 (r/4) + 4 half + r%4,  col = wn*64 + 32 j + l32.
   const float s = p.scale;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = scale_acc(acc[i][j][r], s);
 
   if constexpr (kEpi == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = scale_acc(acc[i][j][r], s);
     // BF16 tile: quarter q (rows 32 q .. 32 q + 31) in the first 8 KB of array q.
     auto put = [&](auto Q) __attribute__((always_inline)) {
       constexpr int q = decltype(Q)::value;
@@ -288,6 +298,7 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
     __syncthreads();
     const int chunk = t & 15, rsub = t >> 4;
     const int64_t gpr = p.N / G;
+    const float s_abs = fabsf(s);
     auto quantize = [&](auto Q) __attribute__((always_inline)) {
       constexpr int qq = decltype(Q)::value;
       const float* ct = reinterpret_cast<const float*>(lds_quarter<qq>());
@@ -301,21 +312,37 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
         const bool ok = m0 + row < p.M;
         if (p.c_f32 && ok) {
           float* dst = p.c_f32 + (m0 + row) * p.N + n0 + col;
-          *reinterpret_cast<float4*>(dst) = v0;
-          *reinterpret_cast<float4*>(dst + 4) = v1;
+          *reinterpret_cast<float4*>(dst) =
+              make_float4(scale_acc(v0.x, s), scale_acc(v0.y, s), scale_acc(v0.z, s), scale_acc(v0.w, s));
+          *reinterpret_cast<float4*>(dst + 4) =
+              make_float4(scale_acc(v1.x, s), scale_acc(v1.y, s), scale_acc(v1.z, s), scale_acc(v1.w, s));
         }
-        float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                         fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+        // The quarters hold the unscaled accumulators c; the group maximum of
+        // |c s| is fl(max |c| * |s|) (rounding is monotone).
+        const float mc = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                               fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
         // non-negative floats order like their bit patterns
-        const float amax = __uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mx)));
-        const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
-        const float rq = 448.0f / (amax * pre);
+        const float amax = scale_acc(__uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mc))), s_abs);
         uint2 c = make_uint2(0u, 0u);
-        if (amax > 0.0f) {
-          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.x * pre, rq), scaled_nz(v0.y * pre, rq), 0, false);
-          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.z * pre, rq), scaled_nz(v0.w * pre, rq), w0, true);
-          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.x * pre, rq), scaled_nz(v1.y * pre, rq), 0, false);
-          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.z * pre, rq), scaled_nz(v1.w * pre, rq), w1, true);
+        if (amax >= 0x1p-100f && amax <= 0x1.fffffep127f) {
+          // code = RNE(c * m), m = fl(s * fl(448 / max)); fma(c, m, +0) folds -0 to +0
+          const float m = scale_acc(448.0f / amax, s);
+          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(v0.x, m, 0.0f), __builtin_fmaf(v0.y, m, 0.0f), 0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(v0.z, m, 0.0f), __builtin_fmaf(v0.w, m, 0.0f), w0, true);
+          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(v1.x, m, 0.0f), __builtin_fmaf(v1.y, m, 0.0f), 0, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(v1.z, m, 0.0f), __builtin_fmaf(v1.w, m, 0.0f), w1, true);
+          c = make_uint2((uint32_t)w0, (uint32_t)w1);
+        } else if (amax > 0.0f) {
+          // maxima below 2^-100 (448 / max would leave FP32's range: scale by
+          // 2^64) or past FP32's range: round c s first, as the definition does
+          const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
+          const float rq = 448.0f / (amax * pre);
+          const float4 x0 = make_float4(scale_acc(v0.x, s), scale_acc(v0.y, s), scale_acc(v0.z, s), scale_acc(v0.w, s));
+          const float4 x1 = make_float4(scale_acc(v1.x, s), scale_acc(v1.y, s), scale_acc(v1.z, s), scale_acc(v1.w, s));
+          int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x0.x * pre, rq), scaled_nz(x0.y * pre, rq), 0, false);
+          w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x0.z * pre, rq), scaled_nz(x0.w * pre, rq), w0, true);
+          int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x1.x * pre, rq), scaled_nz(x1.y * pre, rq), 0, false);
+          w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x1.z * pre, rq), scaled_nz(x1.w * pre, rq), w1, true);
           c = make_uint2((uint32_t)w0, (uint32_t)w1);
         }
         if (ok) {
@@ -333,13 +360,21 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
 
 // ------------------------------------------------------ 256 x 256 tiles
 //
-// The same GEMM with 256 x 256 block tiles: 512 threads, eight waves (2 x 4)
-// of 128 x 64 each (4 x 2 MFMA tiles).  Per unit of output it moves half the
-// panel traffic of the 128 x 128 kernel; the LDS holds 2 stages of 32 KB A
-// and B panels (128 KB), so one block runs per CU.  The epilogue stages the
-// FP32 tile through the same four arrays in two passes of 128 rows (every
-// wave writes two of its four row tiles per pass).  Used when N is a multiple
-// of 256.
+// The same GEMM with 256 x 256 block tiles: 512 threads, eight waves laid
+// out 4 (rows) x 2 (columns), each owning 64 rows x 128 columns as 2 x 4
+// tiles of the 32x32x64 MFMA.  Per unit of output it moves half the panel
+// traffic of the 128 x 128 kernel; the LDS holds 2 stages of 32 KB A and B
+// panels (128 KB), so one block runs per CU.  Used when N is a multiple of
+// 256.
+//
+// The MFMA takes the B panel rows as its first operand, so each 32 x 32
+// result is a tile of C^T: register r of lane l holds C[row][col] with
+// row = 32 i + l % 32 and col = 32 j + 8 (r / 4) + 4 (l / 32) + r % 4 inside
+// the wave's 64 x 128.  A lane therefore holds runs of four consecutive
+// columns, and lanes l and l ^ 32 together hold all 128 columns of two rows.
+// The group maximum of the quantizing epilogue is a reduction over a lane's
+// own registers and one exchange between the half waves; only the finished
+// E4M3 codes go through the LDS, for row-contiguous stores.
 
 constexpr int kBM256 = 256;
 constexpr int kBN256 = 256;
@@ -360,16 +395,34 @@ __device__ __forceinline__ uint8_t* lds256_part() {
   else return lds256_b1;
 }
 
-// Float offset of C[row % 32][col] in a 32-row x 256-column FP32 part, with
-// the same chunk XOR as the 128-column quarters.
-__device__ __forceinline__ int part256_off(int row, int col) {
-  return (row & 31) * kBN256 + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (col & 3);
+__device__ __forceinline__ uint8_t* lds256_part_rt(int q) {
+  return q == 0 ? lds256_a0 : q == 1 ? lds256_b0 : q == 2 ? lds256_a1 : lds256_b1;
+}
+
+// Epilogue staging tiles.  Byte `col` of row `row` of a tile of 256-byte
+// (codes) or 512-byte (BF16) rows, `rows_per_array` rows to a 32 KB array:
+// 16-byte chunks XORed with row % 16, and for the codes the two 8-byte halves
+// of a chunk swapped on rows with bit 4 set.  The writes (32 rows x 8 bytes,
+// or 32 rows x 16 bytes for BF16, per instruction) and the row reads (16 bytes
+// per lane) then meet no bank conflicts.
+__device__ __forceinline__ int code_off(int row, int col) {
+  return (row & 127) * 256 + ((((col >> 4) ^ (row & 15))) << 4) + ((col & 15) ^ (((row >> 4) & 1) << 3));
+}
+__device__ __forceinline__ int bf16_off(int row, int col) {
+  return (row & 63) * 512 + ((((col >> 4) ^ (row & 15))) << 4) + (col & 15);
+}
+
+// Max of x over the lane pair (l, l ^ 32): the exchange returns the pair's
+// two values in either order.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int G, int kEpi>
 __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmParams p) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;   // 2 x 4 waves of 128 x 64
+  const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 waves of 64 x 128
   // Tile order: each XCD takes a contiguous run of tile indices, walked in
   // groups of kGroupM256 tile rows, column by column inside a group, so the A
   // panels of the group stay in the XCD's L2 and each B panel serves kGroupM256
@@ -384,212 +437,303 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
   const int64_t K = p.K;
 
   // Panel loads go straight from global memory into LDS: one wave-wide
-  // 16-byte-per-lane load fills 1 KB, 8 rows of a panel, lane L landing at
-  // byte 16 L.  So lane L carries row R0 + L/8 and the physical chunk L%8,
-  // which under the row swizzle holds logical chunk (L%8) ^ chunk_swz(row);
-  // the swizzle is applied on the global side.  Wave w fills rows 32 w .. 32 w + 31 of each
-  // panel with 4 loads.  Rows of A past M are not loaded (their LDS bytes are
-  // stale and only reach output rows that are never stored).
-  const uint8_t* a_blk = p.a + m0 * K;
-  const uint8_t* b_blk = p.b + n0 * K;
-  uint32_t goff[4];
-  bool a_ok[4];
+  // 16-byte-per-lane buffer load fills 1 KB, 8 rows of a panel, lane L
+  // landing at byte 16 L.  So lane L carries row R0 + L/8 and the physical
+  // chunk L%8, which under the row swizzle holds logical chunk
+  // (L%8) ^ chunk_swz(row); the swizzle is applied on the global side.  Wave
+  // w fills rows 32 w .. 32 w + 31 of each panel with 4 loads.  The buffer
+  // resource holds the panel base, the scalar offset the K position.  A rows
+  // past M re-load row M - 1: their products only reach output rows that are
+  // never stored.  (Buffer loads count only against vmcnt, so the waits for
+  // LDS reads below stay partial while panel loads are in flight.)
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.a + m0 * K), (short)0, (int)0xFFFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b + n0 * K), (short)0, (int)0xFFFFFFFF, 0x00020000);
+  const int64_t a_rows = p.M - m0;
+  uint32_t aoff[4], boff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 32 * wave + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ chunk_swz(row);
-    goff[i] = (uint32_t)row * (uint32_t)K + 16u * (uint32_t)c;
-    a_ok[i] = m0 + row < p.M;
+    const int arow = row < a_rows ? row : (int)(a_rows - 1);
+    aoff[i] = (uint32_t)arow * (uint32_t)K + 16u * (uint32_t)c;
+    boff[i] = (uint32_t)row * (uint32_t)K + 16u * (uint32_t)c;
   }
-  auto issue = [&](int64_t k0, auto S) __attribute__((always_inline)) {
+  // Load q = 0..7 of a K step: A (even q) or B (odd q), rows 32 wave + 8 (q / 2) + lane / 8.
+  auto load1 = [&](int64_t k0, auto S, int q) __attribute__((always_inline)) {
     constexpr int st = decltype(S)::value;
     uint8_t* As = lds256_part<2 * st>();
     uint8_t* Bs = lds256_part<2 * st + 1>();
-    const uint8_t* ak = a_blk + k0;
-    const uint8_t* bk = b_blk + k0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint8_t* dst_a = As + 1024 * (4 * wave + i);
-      uint8_t* dst_b = Bs + 1024 * (4 * wave + i);
-      if (a_ok[i]) __builtin_amdgcn_global_load_lds(ak + goff[i], dst_a, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bk + goff[i], dst_b, 16, 0, 0);
-    }
+    const int i = q >> 1;
+    if (q & 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, Bs + 1024 * (4 * wave + i), 16, (int)boff[i], (int)k0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, As + 1024 * (4 * wave + i), 16, (int)aoff[i], (int)k0, 0, 0);
   };
 
-  v16f acc[4][2];
+  v16f acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int nk = (int)(K / kBK);
   const int half = lane >> 5, l32 = lane & 31;
-  // One K step on stage S: start the loads of step kt + 1 into the other
-  // stage, run the MFMAs on this one, then wait for this wave's loads and
-  // meet the other waves (their loads have landed, nobody reads stage S).
+  // Operand fragment: lane supplies row l32 of a 32-row tile and the k bytes
+  // 64 kk + 32 half .. +31 (logical chunks c0, c0 + 1 of the panel row).
+  auto frag = [&](const uint8_t* panel, int row, int kk) __attribute__((always_inline)) {
+    const int c0 = 4 * kk + 2 * half;
+    const uint4 lo = *reinterpret_cast<const uint4*>(panel + panel_off(row, c0));
+    const uint4 hi = *reinterpret_cast<const uint4*>(panel + panel_off(row, c0 + 1));
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  // A K step is four MFMA groups g = (kk, h): both row tiles against column
+  // tiles 2h, 2h + 1 at k half kk.  The fragments of group g + 1 are read
+  // while the MFMAs of group g run (two register sets fb0 / fb1 for B, one A
+  // set per kk), so the waits on LDS reads are partial.
+  v8i fa0[2], fa1[2], fb0[2], fb1[2];
+  auto read_a = [&](v8i* f, const uint8_t* As, int kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f[i] = frag(As, wm * 64 + 32 * i + l32, kk);
+  };
+  auto read_b = [&](v8i* f, const uint8_t* Bs, int kk, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) f[jj] = frag(Bs, wn * 128 + 32 * (2 * h + jj) + l32, kk);
+  };
+  auto mma1 = [&](const v8i* fa, const v8i* fb, int h, int q) __attribute__((always_inline)) {
+    const int i = q >> 1, jj = q & 1;
+    acc[i][2 * h + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jj], fa[i], acc[i][2 * h + jj],
+                                                                        0, 0, 0, 0, 0, 0);
+  };
+  // The eight panel loads of a K step are spread one per MFMA over three
+  // phases: loads 0-2 of step kt + 2 go out in the last phase of step kt,
+  // right after the barrier that frees stage S; loads 3-7 in the first two
+  // phases of step kt + 1; all are waited for at the barrier of step kt + 1.
+  // Past the last step the loads re-fetch the last K slice into a stage that
+  // is not read again.
+  const int64_t k_last = K - kBK;
+  auto kslice = [&](int k) __attribute__((always_inline)) {
+    return k < nk ? (int64_t)k * kBK : k_last;
+  };
   auto kstep = [&](int kt, auto S) __attribute__((always_inline)) {
     constexpr int st = decltype(S)::value;
-    if (kt + 1 < nk) issue((int64_t)(kt + 1) * kBK, std::integral_constant<int, 1 - st>{});
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+    using N = std::integral_constant<int, 1 - st>;
     const uint8_t* As = lds256_part<2 * st>();
     const uint8_t* Bs = lds256_part<2 * st + 1>();
+    const int64_t k1 = kslice(kt + 1), k2 = kslice(kt + 2);
+    // on entry fa0 / fb0 hold group (0, 0) of stage S
+    read_b(fb1, Bs, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      // lane supplies row (l32) and k bytes 64 kk + 32 half .. +31: chunks c0, c0 + 1
-      const int c0 = 4 * kk + 2 * half;
-      v8i fa[4], fb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + 32 * i + l32;
-        const uint4 lo = *reinterpret_cast<const uint4*>(As + panel_off(row, c0));
-        const uint4 hi = *reinterpret_cast<const uint4*>(As + panel_off(row, c0 + 1));
-        fa[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wn * 64 + 32 * j + l32;
-        const uint4 lo = *reinterpret_cast<const uint4*>(Bs + panel_off(row, c0));
-        const uint4 hi = *reinterpret_cast<const uint4*>(Bs + panel_off(row, c0 + 1));
-        fb[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0,
-                                                                      0, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      mma1(fa0, fb0, 0, q);
+      if (q < 3) load1(k1, N{}, 3 + q);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next panels have landed
+    read_b(fb0, Bs, 1, 0);
+    read_a(fa1, As, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mma1(fa0, fb1, 1, q);
+      if (q < 2) load1(k1, N{}, 6 + q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_b(fb1, Bs, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mma1(fa1, fb0, 0, q);
+    __builtin_amdgcn_sched_barrier(0);
+    // every wave has read all of stage S and waits for its loads of stage
+    // 1 - S; after the barrier stage 1 - S is complete and stage S is free
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // first fragments of the next step (after the last step: read, unused)
+    read_b(fb0, lds256_part<2 * (1 - st) + 1>(), 0, 0);
+    read_a(fa0, lds256_part<2 * (1 - st)>(), 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mma1(fa1, fb1, 1, q);
+      if (q < 3) load1(k2, S, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  if (nk > 0) issue(0, std::integral_constant<int, 0>{});
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (nk > 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load1(0, std::integral_constant<int, 0>{}, q);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) load1(kslice(1), std::integral_constant<int, 1>{}, q);
+    read_b(fb0, lds256_part<1>(), 0, 0);
+    read_a(fa0, lds256_part<0>(), 0);
+  }
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     kstep(kt, std::integral_constant<int, 0>{});
     kstep(kt + 1, std::integral_constant<int, 1>{});
   }
   if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);  // loads past the last step; the epilogue reuses the arrays
+  __syncthreads();
 
-  // Epilogue.  Value (i, j, r) of this lane is C[row][col] with
-  //   row = wm*64 + 32 i + 8 (r/4) + 4 half + r%4,  col = wn*64 + 32 j + l32.
+  // Epilogue.  Register 4 q + s of acc[i][j] is C[row][col] with
+  //   row = wm * 64 + 32 i + l32,  col = wn * 128 + 32 j + 8 q + 4 half + s.
   const float s = p.scale;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = scale_acc(acc[i][j][r], s);
-
   if constexpr (kEpi == kBF16) {
-    // BF16 tile: array q holds rows 64 q .. 64 q + 63 (64 x 256 x 2 bytes).
-    auto put = [&](auto Q) __attribute__((always_inline)) {
-      constexpr int q = decltype(Q)::value;
-      uint16_t* tile = reinterpret_cast<uint16_t*>(lds256_part<q>());
-      if (wm == (q >> 1)) {
+    // BF16 tile, 64 rows x 512 bytes per array: a lane writes its runs of
+    // four columns (8 bytes), then every lane stores 16-byte row chunks.
+    uint8_t* wtile = lds256_part_rt(wm);
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * (q & 1) + ii;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = 32 * ii + 8 * (r >> 2) + 4 * half + (r & 3);
-              tile[row * kBN256 + wn * 64 + 32 * j + l32] = bf16_rne(acc[i][j][r]);
-            }
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * 64 + 32 * i + l32;
+          const int col = 2 * (wn * 128 + 32 * j + 8 * q + 4 * half);
+          const uint32_t lo = bf16_rne(scale_acc(acc[i][j][4 * q], s)) |
+                              ((uint32_t)bf16_rne(scale_acc(acc[i][j][4 * q + 1], s)) << 16);
+          const uint32_t hi = bf16_rne(scale_acc(acc[i][j][4 * q + 2], s)) |
+                              ((uint32_t)bf16_rne(scale_acc(acc[i][j][4 * q + 3], s)) << 16);
+          *reinterpret_cast<uint2*>(wtile + bf16_off(row, col)) = make_uint2(lo, hi);
         }
-      }
-    };
-    auto get = [&](auto Q) __attribute__((always_inline)) {
-      constexpr int q = decltype(Q)::value;
-      const uint16_t* tile = reinterpret_cast<const uint16_t*>(lds256_part<q>());
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qq = t + kThreads256 * i, row = qq >> 5, c = qq & 31;
-        if (m0 + 64 * q + row < p.M) {
-          const uint4 v = *reinterpret_cast<const uint4*>(tile + row * kBN256 + 8 * c);
-          *reinterpret_cast<uint4*>(p.c_bf16 + (m0 + 64 * q + row) * p.N + n0 + 8 * c) = v;
-        }
-      }
-    };
-    put(std::integral_constant<int, 0>{});
-    put(std::integral_constant<int, 1>{});
-    put(std::integral_constant<int, 2>{});
-    put(std::integral_constant<int, 3>{});
     __syncthreads();
-    get(std::integral_constant<int, 0>{});
-    get(std::integral_constant<int, 1>{});
-    get(std::integral_constant<int, 2>{});
-    get(std::integral_constant<int, 3>{});
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int task = k * kThreads256 + t, row = task >> 5, c = task & 31;
+      const uint8_t* rtile = lds256_part_rt(row >> 6);
+      const uint4 v = *reinterpret_cast<const uint4*>(rtile + bf16_off(row, 16 * c));
+      if (m0 + row < p.M)
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(p.c_bf16 + (m0 + row) * p.N + n0) + 16 * c) = v;
+    }
   } else {
-    const int chunk = t & 31, rsub = t >> 5;
+    constexpr int kGW = 128 / G;   // groups per row in the wave's 128 columns
     const int64_t gpr = p.N / G;
-    auto pass = [&](auto P) __attribute__((always_inline)) {
-      constexpr int ps = decltype(P)::value;
-      // Every wave writes its row tiles i = 2 ps, 2 ps + 1: array k holds the
-      // 32 rows 128 (k / 2) + 32 ((k % 2) + 2 ps) .. + 31 of the tile.
-      auto put = [&](auto Q) __attribute__((always_inline)) {
-        constexpr int ii = decltype(Q)::value;           // 0, 1
-        constexpr int i = 2 * ps + ii;
+    const float s_abs = fabsf(s);
+    // optional FP32 copy of C
+    if (p.c_f32) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 2; ++i) {
+        const int64_t row = m0 + wm * 64 + 32 * i + l32;
+        if (row < p.M) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 8 * (r >> 2) + 4 * half + (r & 3);
-            const int off = part256_off(row, wn * 64 + 32 * j + l32);
-            if (wm == 0) reinterpret_cast<float*>(lds256_part<ii>())[off] = acc[i][j][r];
-            else reinterpret_cast<float*>(lds256_part<2 + ii>())[off] = acc[i][j][r];
-          }
-      };
-      put(std::integral_constant<int, 0>{});
-      put(std::integral_constant<int, 1>{});
-      __syncthreads();
-      auto quantize = [&](auto Q) __attribute__((always_inline)) {
-        constexpr int qq = decltype(Q)::value;
-        const float* ct = reinterpret_cast<const float*>(lds256_part<qq>());
+          for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int lrow = 16 * h2 + rsub;              // row inside the array
-          const int row = 128 * (qq >> 1) + 32 * ((qq & 1) + 2 * ps) + lrow;  // row inside the tile
-          const int col = 8 * chunk;
-          const float4 v0 = *reinterpret_cast<const float4*>(ct + part256_off(lrow, col));
-          const float4 v1 = *reinterpret_cast<const float4*>(ct + part256_off(lrow, col + 4));
-          const bool ok = m0 + row < p.M;
-          if (p.c_f32 && ok) {
-            float* dst = p.c_f32 + (m0 + row) * p.N + n0 + col;
-            *reinterpret_cast<float4*>(dst) = v0;
-            *reinterpret_cast<float4*>(dst + 4) = v1;
-          }
-          float mx = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                           fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-          const float amax = __uint_as_float(lanes_max_u32<G / 8>(__float_as_uint(mx)));
-          const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
-          const float rq = 448.0f / (amax * pre);
-          uint2 c = make_uint2(0u, 0u);
-          if (amax > 0.0f) {
-            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.x * pre, rq), scaled_nz(v0.y * pre, rq), 0, false);
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v0.z * pre, rq), scaled_nz(v0.w * pre, rq), w0, true);
-            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.x * pre, rq), scaled_nz(v1.y * pre, rq), 0, false);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(v1.z * pre, rq), scaled_nz(v1.w * pre, rq), w1, true);
-            c = make_uint2((uint32_t)w0, (uint32_t)w1);
-          }
-          if (ok) {
-            *reinterpret_cast<uint2*>(p.codes + (m0 + row) * p.N + n0 + col) = c;
-            if (chunk % (G / 8) == 0) p.scales[(m0 + row) * gpr + (n0 + col) / G] = amax / 448.0f;
-          }
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(p.c_f32 + row * p.N + n0 + wn * 128 + 32 * j + 8 * q + 4 * half) =
+                  make_float4(scale_acc(acc[i][j][4 * q], s), scale_acc(acc[i][j][4 * q + 1], s),
+                              scale_acc(acc[i][j][4 * q + 2], s), scale_acc(acc[i][j][4 * q + 3], s));
         }
-      };
-      quantize(std::integral_constant<int, 0>{});
-      quantize(std::integral_constant<int, 1>{});
-      quantize(std::integral_constant<int, 2>{});
-      quantize(std::integral_constant<int, 3>{});
-    };
-    pass(std::integral_constant<int, 0>{});
-    __syncthreads();   // the arrays are rewritten by the second pass
-    pass(std::integral_constant<int, 1>{});
+      }
+    }
+    // Group maxima of |c| (c the unscaled accumulator): stage one over the
+    // lane's registers of the group, stage two over the lane pair.  The group
+    // maximum of |c s| is then fl(max |c| * |s|): rounding is monotone.
+    float amax[2][kGW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < kGW; ++g) amax[i][g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int g = (32 * j + 8 * q) / G;
+          amax[i][g] = fmaxf(fmaxf(amax[i][g], fmaxf(fabsf(acc[i][j][4 * q]), fabsf(acc[i][j][4 * q + 1]))),
+                             fmaxf(fabsf(acc[i][j][4 * q + 2]), fabsf(acc[i][j][4 * q + 3])));
+        }
+    // Per group: the stored scale max / 448 and the multiplier m with
+    // code = RNE(c * m), m = fl(s * fl(448 / max)).  Groups whose max lies
+    // outside [2^-100, FLT_MAX] (and zero groups) get m = 0 here and are
+    // handled below.
+    float mul[2][kGW];
+    bool slow = false;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < kGW; ++g) {
+        amax[i][g] = scale_acc(pair_max(amax[i][g]), s_abs);
+        const bool fast = amax[i][g] >= 0x1p-100f && amax[i][g] <= 0x1.fffffep127f;
+        mul[i][g] = fast ? scale_acc(448.0f / amax[i][g], s) : 0.0f;
+        slow |= !fast && amax[i][g] > 0.0f;
+      }
+    uint32_t word[2][4][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float m = mul[i][(32 * j + 8 * q) / G];
+          // fma(c, m, +0) folds an exact -0 product to +0
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(acc[i][j][4 * q], m, 0.0f),
+                                                  __builtin_fmaf(acc[i][j][4 * q + 1], m, 0.0f), 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(acc[i][j][4 * q + 2], m, 0.0f),
+                                              __builtin_fmaf(acc[i][j][4 * q + 3], m, 0.0f), w, true);
+          word[i][j][q] = (uint32_t)w;
+        }
+    if (slow) {
+      // Maxima below 2^-100 (448 / max would leave FP32's range: scale by
+      // 2^64) or past FP32's range: round c s first, as the definition does.
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float am = amax[i][(32 * j + 8 * q) / G];
+            if (!(am >= 0x1p-100f && am <= 0x1.fffffep127f) && am > 0.0f) {
+              const float pre = am < 0x1p-100f ? 0x1p64f : 1.0f;
+              const float rq = 448.0f / (am * pre);
+              const float x0 = scale_acc(acc[i][j][4 * q], s), x1 = scale_acc(acc[i][j][4 * q + 1], s);
+              const float x2 = scale_acc(acc[i][j][4 * q + 2], s), x3 = scale_acc(acc[i][j][4 * q + 3], s);
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x0 * pre, rq), scaled_nz(x1 * pre, rq), 0, false);
+              w = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x2 * pre, rq), scaled_nz(x3 * pre, rq), w, true);
+              word[i][j][q] = (uint32_t)w;
+            }
+          }
+    }
+    // scales: the pair shares each maximum; half h stores groups g % 2 == h
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = m0 + wm * 64 + 32 * i + l32;
+      if (row < p.M) {
+#pragma unroll
+        for (int g = 0; g < kGW; ++g)
+          if (kGW == 1 ? half == 0 : (g & 1) == half)
+            p.scales[row * gpr + (n0 + wn * 128) / G + g] = amax[i][g] / 448.0f;
+      }
+    }
+    // codes through the LDS (256 rows x 256 bytes in two arrays), then
+    // 16-byte row chunks to global memory
+    uint8_t* wtile = wm < 2 ? lds256_a0 : lds256_b0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * 64 + 32 * i + l32;
+          const int col = wn * 128 + 32 * j + 8 * q + 4 * half;
+          *reinterpret_cast<uint32_t*>(wtile + code_off(row, col)) = word[i][j][q];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int task = k * kThreads256 + t, row = task >> 4, c = task & 15;
+      const uint8_t* rtile = row < 128 ? lds256_a0 : lds256_b0;
+      // chunk base (the 8-byte halves are swapped on rows with bit 4 set)
+      uint4 v = *reinterpret_cast<const uint4*>(rtile + (row & 127) * 256 + ((c ^ (row & 15)) << 4));
+      if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      if (m0 + row < p.M) *reinterpret_cast<uint4*>(p.codes + (m0 + row) * p.N + n0 + 16 * c) = v;
+    }
   }
 }
 

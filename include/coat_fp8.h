@@ -177,18 +177,23 @@ coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows,
  * the GEMM output viewed as (BLOCK_M, BLOCK_N/G, G) with the max taken along
  * the last axis; section 四 table, 组缩放技术: a two-stage max reduction fused
  * into the producing operation; [P1] 核心公式 FP8量化 with S = max|X| / 448).
- *   C = (a_scale * b_scale) * A B^T, accumulated in FP32 on the matrix cores,
- *   then each 1xG group of a row of C is quantized like coat_fp8_quantize_act
- *   does (r = 448 / max and C * r rounded to FP32, RNE to E4M3, -0 -> 0x00,
- *   all-zero group -> S = 0 and codes 0).
+ *   C = s * A B^T with s = a_scale * b_scale, accumulated in FP32 on the
+ *   matrix cores as c = A B^T, then each 1xG group of a row of C is
+ *   quantized: S = max|c s| / 448 with max|c s| = fl(max|c| * |s|), and each
+ *   code RNE_E4M3(c * m) with m = fl(s * fl(448 / max)) rounded once to FP32
+ *   (-0 -> 0x00, all-zero group -> S = 0 and codes 0).  This equals the
+ *   quantizer of coat_fp8_quantize_act applied to fl(c s) bit for bit when s
+ *   is a power of two, and otherwise to within one FP32 rounding of the
+ *   value rounded to E4M3; groups whose max lies below 2^-100 or beyond FP32
+ *   are quantized from fl(c s) exactly as coat_fp8_quantize_act does.
  *   a        M x K E4M3 codes, row-major (read only).
  *   b        N x K E4M3 codes, row-major (read only): the weight of a linear
  *            layer y = x W^T in its usual [out, in] layout.
- *   a_scale, b_scale  per-tensor scales, finite; their product is rounded to
- *            FP32 once and multiplies the FP32 accumulators.
+ *   a_scale, b_scale  per-tensor scales, finite; their product s is
+ *            rounded to FP32 once.
  *   codes    M x N E4M3 codes, row-major (written).
  *   scales   M x (N / group_size) FP32, row-major (written).
- *   c_f32    optional M x N FP32 C before quantization (written), or NULL.
+ *   c_f32    optional M x N FP32 fl(c s) before quantization (written), or NULL.
  * N and K must be multiples of 128, K <= 2^24; M is any size >= 0 (M or N
  * zero is a no-op; K zero gives C = 0, and a, b may then be NULL).  a, b,
  * codes and c_f32 16-byte aligned, scales 4-byte aligned.  NaN codes in a or

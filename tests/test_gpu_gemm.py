@@ -27,6 +27,7 @@ import torch
 import oracle
 from adamw_coat_fp8_amd import inputs
 from gpu_util import DEV, lib, require_gpu
+from parity import signed_ordinal
 
 pytestmark = pytest.mark.gpu
 
@@ -77,6 +78,65 @@ def test_exact_inputs_bit_exact(G, shape):
                                                           sa, sb, G, want_c=True)
     assert np.all(c64 == c32)                       # the inputs keep C exact in FP32
     _assert_bit_exact(f"exact {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
+
+
+# one shape per kernel: N = 384 takes the 128 x 128 tiles, N = 512 the 256 x 256 ones
+SCALE_SHAPES = [(100, 384, 256), (96, 512, 512)]
+
+
+@pytest.mark.parametrize("G", [16, 128])
+@pytest.mark.parametrize("shape", SCALE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SCALE_SHAPES])
+def test_folded_multiplier_exact_inputs(G, shape):
+    """A scale product s that is not a power of two (0.1 * 3.0), on exact
+    integer-valued accumulators c: the scales are fl(max|c| |s|) / 448 and the
+    codes RNE(c * m) with m = fl(s * fl(448 / max)), bit for bit (FP32 steps
+    emulated in numpy, E4M3 rounding by the oracle's encoder).  Against the
+    definition (the oracle, which multiplies by the exact product of the two
+    scales) the scales agree to two FP32 roundings and the codes are at most
+    one E4M3 step away."""
+    M, N, K = shape
+    a, b, _, _ = inputs.fp8_operands(M, N, K, 4, DEV, "exact")
+    sa, sb = 0.1, 3.0
+    print(f"[gemm] folded multiplier {M}x{N}x{K} G={G}", flush=True)
+    gc, gs, _ = _run(a, b, sa, sb, G, want_c=False)
+    an, bn = a.cpu().numpy(), b.cpu().numpy()
+    c = oracle.e4m3_decode_array(an).reshape(an.shape) @ oracle.e4m3_decode_array(bn).reshape(bn.shape).T
+    c32 = c.astype(np.float32)
+    assert np.all(c32 == c)                          # integer sums below 2^24
+    s = np.float32(np.float32(sa) * np.float32(sb))
+    amax = np.abs(c32).reshape(M, N // G, G).max(-1) * np.abs(s)
+    assert amax.dtype == np.float32 and np.all((amax == 0) | (amax >= 2.0 ** -100))
+    want_s = amax / np.float32(448.0)
+    assert np.array_equal(gs.view(np.uint32), want_s.view(np.uint32))
+    with np.errstate(divide="ignore"):
+        m = np.where(amax > 0, s * (np.float32(448.0) / amax), np.float32(0.0)).astype(np.float32)
+    q = c32.reshape(M, N // G, G) * m[..., None] + np.float32(0.0)
+    want_c = oracle.e4m3_encode_array(q.reshape(-1).astype(np.float64)).reshape(M, N)
+    bad = np.argwhere(gc != want_c)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}"
+    # the oracle multiplies by the exact product of the two scales, the
+    # library by that product rounded to FP32: the scales agree to two roundings
+    rc, rs = oracle.gemm_fp8_group_quant(an, bn, sa, sb, G)
+    assert np.all(np.abs(gs.astype(np.float64) - rs) <= 2.0 ** -22 * rs)
+    step = np.abs(signed_ordinal(gc).astype(np.int64) - signed_ordinal(rc).astype(np.int64))
+    print(f"[gemm] folded multiplier: {np.mean(step == 0):.6f} of codes as the definition's", flush=True)
+    assert step.max() <= 1
+
+
+@pytest.mark.parametrize("G", [16, 128])
+@pytest.mark.parametrize("shape", SCALE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SCALE_SHAPES])
+def test_tiny_scale_product(G, shape):
+    """s = 2^-120: every group maximum lies below 2^-100, where 448 / max
+    leaves FP32's range; those groups are quantized from fl(c s) with the
+    2^64 pre-scale, bit for bit as the oracle does."""
+    M, N, K = shape
+    a, b, _, _ = inputs.fp8_operands(M, N, K, 5, DEV, "exact")
+    sa = sb = 2.0 ** -60
+    print(f"[gemm] tiny scale product {M}x{N}x{K} G={G}", flush=True)
+    codes, scales, c64, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(),
+                                                          sa, sb, G, want_c=True)
+    assert np.all(c64 == c32) and np.max(np.abs(c32)) < 2.0 ** -100
+    _assert_bit_exact(f"tiny scale {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
 
 
 def _interval_check(tag, a, b, sa, sb, G, gpu, rows=None):

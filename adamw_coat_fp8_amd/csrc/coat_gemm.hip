@@ -91,7 +91,8 @@ struct GemmParams {
   float* c_f32;      // optional M x N FP32 C (group quant)
   uint16_t* c_bf16;  // M x N BF16 (plain epilogue)
   int64_t M, N, K;
-  int64_t n_tiles;   // N / 128
+  int64_t n_tiles;   // N / 128 (N / 256 for the 256 x 256 kernel)
+  int64_t tile_base; // first tile of this launch in the tile order (256 x 256 kernel)
   float scale;       // a_scale * b_scale, rounded to FP32
 };
 
@@ -365,7 +366,9 @@ __global__ __launch_bounds__(kBlockThreads) void gemm_fp8_kernel(const GemmParam
 // tiles of the 32x32x64 MFMA.  Per unit of output it moves half the panel
 // traffic of the 128 x 128 kernel; the LDS holds 2 stages of 32 KB A and B
 // panels (128 KB), so one block runs per CU.  Used when N is a multiple of
-// 256.
+// 256.  With kI = 1 a block computes half a tile, 128 x 256 (waves of
+// 32 x 128): when the tiles do not fill the last round of CUs, the last
+// tiles of the order run as two halves each in a second launch.
 //
 // The MFMA takes the B panel rows as its first operand, so each 32 x 32
 // result is a tile of C^T: register r of lane l holds C[row][col] with
@@ -419,21 +422,26 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int G, int kEpi>
+template <int G, int kEpi, int kI>
 __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmParams p) {
+  static_assert(kI == 1 || kI == 2, "row tiles per wave");
+  constexpr int kWaveRows = 32 * kI;         // rows of C per wave (128 kI per block)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 waves of 64 x 128
+  const int wm = wave & 3, wn = wave >> 2;   // 4 x 2 waves of kWaveRows x 128
   // Tile order: each XCD takes a contiguous run of tile indices, walked in
   // groups of kGroupM256 tile rows, column by column inside a group, so the A
   // panels of the group stay in the XCD's L2 and each B panel serves kGroupM256
   // tiles in a row.
-  const int64_t bid = xcd_contiguous(blockIdx.x, gridDim.x);
+  // (half tiles: the two halves of a tile are neighbours in the order)
+  const int64_t bidx = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int64_t bid = p.tile_base + (kI == 2 ? bidx : bidx >> 1);
   const int64_t m_tiles = (p.M + kBM256 - 1) / kBM256;
   const int64_t group = bid / (kGroupM256 * p.n_tiles), first_m = group * kGroupM256;
   const int64_t gm = m_tiles - first_m < kGroupM256 ? m_tiles - first_m : kGroupM256;
   const int64_t local = bid - group * kGroupM256 * p.n_tiles;
   const int64_t tm = first_m + local % gm, tn = local / gm;
-  const int64_t m0 = tm * kBM256, n0 = tn * kBN256;
+  const int64_t m0 = tm * kBM256 + (kI == 2 ? 0 : 128 * (bidx & 1)), n0 = tn * kBN256;
+  if (m0 >= p.M) return;   // second half of a last tile row of at most 128 rows
   const int64_t K = p.K;
 
   // Panel loads go straight from global memory into LDS: one wave-wide
@@ -460,7 +468,9 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
     aoff[i] = (uint32_t)arow * (uint32_t)K + 16u * (uint32_t)c;
     boff[i] = (uint32_t)row * (uint32_t)K + 16u * (uint32_t)c;
   }
-  // Load q = 0..7 of a K step: A (even q) or B (odd q), rows 32 wave + 8 (q / 2) + lane / 8.
+  // Load q = 0..7 of a K step: A (even q) or B (odd q), rows 32 wave + 8 (q / 2) + lane / 8
+  // (a half tile's A panel has 128 rows: waves 0-3 load it).
+  const bool a_loader = kI == 2 || wave < 4;
   auto load1 = [&](int64_t k0, auto S, int q) __attribute__((always_inline)) {
     constexpr int st = decltype(S)::value;
     uint8_t* As = lds256_part<2 * st>();
@@ -468,13 +478,13 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
     const int i = q >> 1;
     if (q & 1)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, Bs + 1024 * (4 * wave + i), 16, (int)boff[i], (int)k0, 0, 0);
-    else
+    else if (a_loader)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, As + 1024 * (4 * wave + i), 16, (int)aoff[i], (int)k0, 0, 0);
   };
 
-  v16f acc[2][4];
+  v16f acc[kI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -494,19 +504,22 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
   // tiles 2h, 2h + 1 at k half kk.  The fragments of group g + 1 are read
   // while the MFMAs of group g run (two register sets fb0 / fb1 for B, one A
   // set per kk), so the waits on LDS reads are partial.
-  v8i fa0[2], fa1[2], fb0[2], fb1[2];
+  v8i fa0[kI], fa1[kI], fb0[2], fb1[2];
   auto read_a = [&](v8i* f, const uint8_t* As, int kk) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f[i] = frag(As, wm * 64 + 32 * i + l32, kk);
+    for (int i = 0; i < kI; ++i) f[i] = frag(As, wm * kWaveRows + 32 * i + l32, kk);
   };
   auto read_b = [&](v8i* f, const uint8_t* Bs, int kk, int h) __attribute__((always_inline)) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) f[jj] = frag(Bs, wn * 128 + 32 * (2 * h + jj) + l32, kk);
   };
+  // MFMA q (0 .. 2 kI - 1) of a group: row tile q / 2, column tile 2 h + q % 2
   auto mma1 = [&](const v8i* fa, const v8i* fb, int h, int q) __attribute__((always_inline)) {
-    const int i = q >> 1, jj = q & 1;
-    acc[i][2 * h + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jj], fa[i], acc[i][2 * h + jj],
-                                                                        0, 0, 0, 0, 0, 0);
+    if (q < 2 * kI) {
+      const int i = q >> 1, jj = q & 1;
+      acc[i][2 * h + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jj], fa[i], acc[i][2 * h + jj],
+                                                                          0, 0, 0, 0, 0, 0);
+    }
   };
   // The eight panel loads of a K step are spread one per MFMA over three
   // phases: loads 0-2 of step kt + 2 go out in the last phase of step kt,
@@ -582,19 +595,19 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
   __syncthreads();
 
   // Epilogue.  Register 4 q + s of acc[i][j] is C[row][col] with
-  //   row = wm * 64 + 32 i + l32,  col = wn * 128 + 32 j + 8 q + 4 half + s.
+  //   row = wm * kWaveRows + 32 i + l32,  col = wn * 128 + 32 j + 8 q + 4 half + s.
   const float s = p.scale;
   if constexpr (kEpi == kBF16) {
     // BF16 tile, 64 rows x 512 bytes per array: a lane writes its runs of
     // four columns (8 bytes), then every lane stores 16-byte row chunks.
-    uint8_t* wtile = lds256_part_rt(wm);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + 32 * i + l32;
+          const int row = wm * kWaveRows + 32 * i + l32;
+          uint8_t* wtile = lds256_part_rt((wm * kWaveRows + 32 * i) >> 6);
           const int col = 2 * (wn * 128 + 32 * j + 8 * q + 4 * half);
           const uint32_t lo = bf16_rne(scale_acc(acc[i][j][4 * q], s)) |
                               ((uint32_t)bf16_rne(scale_acc(acc[i][j][4 * q + 1], s)) << 16);
@@ -604,7 +617,7 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
         }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 8 * kI; ++k) {
       const int task = k * kThreads256 + t, row = task >> 5, c = task & 31;
       const uint8_t* rtile = lds256_part_rt(row >> 6);
       const uint4 v = *reinterpret_cast<const uint4*>(rtile + bf16_off(row, 16 * c));
@@ -618,8 +631,8 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
     // optional FP32 copy of C
     if (p.c_f32) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t row = m0 + wm * 64 + 32 * i + l32;
+      for (int i = 0; i < kI; ++i) {
+        const int64_t row = m0 + wm * kWaveRows + 32 * i + l32;
         if (row < p.M) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
@@ -634,13 +647,13 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
     // Group maxima of |c| (c the unscaled accumulator): stage one over the
     // lane's registers of the group, stage two over the lane pair.  The group
     // maximum of |c s| is then fl(max |c| * |s|): rounding is monotone.
-    float amax[2][kGW];
+    float amax[kI][kGW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int g = 0; g < kGW; ++g) amax[i][g] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -653,10 +666,10 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
     // code = RNE(c * m), m = fl(s * fl(448 / max)).  Groups whose max lies
     // outside [2^-100, FLT_MAX] (and zero groups) get m = 0 here and are
     // handled below.
-    float mul[2][kGW];
+    float mul[kI][kGW];
     bool slow = false;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int g = 0; g < kGW; ++g) {
         amax[i][g] = scale_acc(pair_max(amax[i][g]), s_abs);
@@ -664,9 +677,9 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
         mul[i][g] = fast ? scale_acc(448.0f / amax[i][g], s) : 0.0f;
         slow |= !fast && amax[i][g] > 0.0f;
       }
-    uint32_t word[2][4][4];
+    uint32_t word[kI][4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -683,7 +696,7 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
       // Maxima below 2^-100 (448 / max would leave FP32's range: scale by
       // 2^64) or past FP32's range: round c s first, as the definition does.
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -702,8 +715,8 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
     }
     // scales: the pair shares each maximum; half h stores groups g % 2 == h
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t row = m0 + wm * 64 + 32 * i + l32;
+    for (int i = 0; i < kI; ++i) {
+      const int64_t row = m0 + wm * kWaveRows + 32 * i + l32;
       if (row < p.M) {
 #pragma unroll
         for (int g = 0; g < kGW; ++g)
@@ -711,22 +724,22 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
             p.scales[row * gpr + (n0 + wn * 128) / G + g] = amax[i][g] / 448.0f;
       }
     }
-    // codes through the LDS (256 rows x 256 bytes in two arrays), then
-    // 16-byte row chunks to global memory
-    uint8_t* wtile = wm < 2 ? lds256_a0 : lds256_b0;
+    // codes through the LDS (128 kI rows x 256 bytes, 128 rows per array),
+    // then 16-byte row chunks to global memory
+    uint8_t* wtile = wm * kWaveRows < 128 ? lds256_a0 : lds256_b0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + 32 * i + l32;
+          const int row = wm * kWaveRows + 32 * i + l32;
           const int col = wn * 128 + 32 * j + 8 * q + 4 * half;
           *reinterpret_cast<uint32_t*>(wtile + code_off(row, col)) = word[i][j][q];
         }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4 * kI; ++k) {
       const int task = k * kThreads256 + t, row = task >> 4, c = task & 15;
       const uint8_t* rtile = row < 128 ? lds256_a0 : lds256_b0;
       // chunk base (the 8-byte halves are swapped on rows with bit 4 set)
@@ -737,21 +750,21 @@ __global__ __launch_bounds__(kThreads256) void gemm_fp8_kernel_256(const GemmPar
   }
 }
 
-template <int G>
-const void* gq_fn(bool big) {
-  return big ? reinterpret_cast<const void*>(&gemm_fp8_kernel_256<G, kGroupQuant>)
-             : reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kGroupQuant>);
+// Kernel for a tile shape: 0 = 128 x 128, 1 = 256 x 256, 2 = 128 x 256 half tiles.
+template <int G, int kEpi>
+const void* kernel_fn(int shape) {
+  if (shape == 1) return reinterpret_cast<const void*>(&gemm_fp8_kernel_256<G, kEpi, 2>);
+  if (shape == 2) return reinterpret_cast<const void*>(&gemm_fp8_kernel_256<G, kEpi, 1>);
+  return reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kEpi>);
 }
 
-const void* gemm_kernel_for(int32_t g, int epi, bool big) {
-  if (epi == kBF16)
-    return big ? reinterpret_cast<const void*>(&gemm_fp8_kernel_256<128, kBF16>)
-               : reinterpret_cast<const void*>(&gemm_fp8_kernel<128, kBF16>);
+const void* gemm_kernel_for(int32_t g, int epi, int shape) {
+  if (epi == kBF16) return kernel_fn<128, kBF16>(shape);
   switch (g) {
-    case 16: return gq_fn<16>(big);
-    case 32: return gq_fn<32>(big);
-    case 64: return gq_fn<64>(big);
-    default: return gq_fn<128>(big);
+    case 16: return kernel_fn<16, kGroupQuant>(shape);
+    case 32: return kernel_fn<32, kGroupQuant>(shape);
+    case 64: return kernel_fn<64, kGroupQuant>(shape);
+    default: return kernel_fn<128, kGroupQuant>(shape);
   }
 }
 
@@ -768,15 +781,36 @@ coat_status_t check_gemm_shape(const uint8_t* a, const uint8_t* b, float a_scale
   return COAT_OK;
 }
 
-// 256 x 256 tiles when N allows them (N % 256 == 0), else 128 x 128.
+// 256 x 256 tiles when N allows them (N % 256 == 0), else 128 x 128.  One
+// 256 x 256 block runs per CU.  When the tiles leave the last round of CUs
+// at most half full, the whole rounds run as 256 x 256 tiles and the
+// remaining tiles of the order as two 128 x 256 halves each, in a second
+// launch on the same stream: half a round instead of a full one.
 hipError_t launch_gemm(GemmParams& p, int32_t group_size, int epi, hipStream_t stream) {
-  const bool big = p.N % kBN256 == 0;
-  const int64_t bm = big ? kBM256 : kBM, bn = big ? kBN256 : kBN;
-  p.n_tiles = p.N / bn;
-  const int64_t blocks = (p.M + bm - 1) / bm * p.n_tiles;
   void* args[] = {&p};
-  return hipLaunchKernel(gemm_kernel_for(group_size, epi, big), dim3((unsigned)blocks),
-                         dim3(big ? kThreads256 : kBlockThreads), args, 0, stream);
+  if (p.N % kBN256 != 0) {
+    p.n_tiles = p.N / kBN;
+    const int64_t blocks = (p.M + kBM - 1) / kBM * p.n_tiles;
+    return hipLaunchKernel(gemm_kernel_for(group_size, epi, 0), dim3((unsigned)blocks),
+                           dim3(kBlockThreads), args, 0, stream);
+  }
+  p.n_tiles = p.N / kBN256;
+  const int64_t tiles = (p.M + kBM256 - 1) / kBM256 * p.n_tiles;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t rem = cus > 0 ? tiles % cus : 0;
+  const int64_t whole = rem > 0 && 2 * rem <= cus ? tiles - rem : tiles;
+  p.tile_base = 0;
+  if (whole > 0) {
+    e = hipLaunchKernel(gemm_kernel_for(group_size, epi, 1), dim3((unsigned)whole), dim3(kThreads256),
+                        args, 0, stream);
+    if (e != hipSuccess || whole == tiles) return e;
+  }
+  p.tile_base = whole;
+  return hipLaunchKernel(gemm_kernel_for(group_size, epi, 2), dim3((unsigned)(2 * (tiles - whole))),
+                         dim3(kThreads256), args, 0, stream);
 }
 
 }  // namespace

@@ -366,6 +366,22 @@ def cpu_baseline_gemm(a, b, sa, sb, G, min_seconds=10.0):
                       f"sums), {passes} passes after an untimed one, {dt:.2f} s wall"}
 
 
+def gemm_tiling(M, N):
+    """The library's tile plan for an M x N output: 128 x 128 tiles unless N
+    is a multiple of 256; then 256 x 256 tiles, with the tiles of a last round
+    that would leave over half the CUs idle run as 128 x 256 halves in a
+    second launch."""
+    import torch
+    if N % 256:
+        return "128x128"
+    tiles = -(-M // 256) * (N // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rem = tiles % cus
+    if rem == 0 or 2 * rem > cus:
+        return f"256x256 ({tiles} tiles)"
+    return f"256x256 ({tiles - rem} tiles) + 128x256 halves of the last {rem} tiles (second launch)"
+
+
 def bench_gemm(args):
     import torch
     from adamw_coat_fp8_amd import coat, inputs
@@ -415,7 +431,7 @@ def bench_gemm(args):
                "group_epilogue_overhead": round(ms_launch / ms_plain - 1.0, 4),
                "unfused_bf16_gemm_then_quantizer_ms": round(ms_unfused, 5),
                "fused_saving_vs_unfused": round(1.0 - ms_launch / ms_unfused, 4),
-               "tile": "256x256" if N % 256 == 0 else "128x128"}
+               "tile": gemm_tiling(M, N)}
     # a library FP8 GEMM (hipBLASLt through torch) for context, if this build has one
     try:
         af = a.view(torch.float8_e4m3fn)
@@ -465,7 +481,8 @@ def bench_gemm(args):
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"gemm_fp8_kernel<{G}, group quant>",
+            "kernel": (f"gemm_fp8_kernel_256<{G}, group quant> (with its half-tile launch, if any: "
+                       f"times are per library call)" if N % 256 == 0 else f"gemm_fp8_kernel<{G}, group quant>"),
             "flops_per_launch": flops,
             "avg_launch_ms": round(ms_launch, 5),
         },

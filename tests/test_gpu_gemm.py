@@ -282,6 +282,28 @@ def test_bf16_epilogue(shape):
     assert np.array_equal(c.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("G", [16, 128])
+def test_whole_rounds_and_half_tiles(G):
+    """4000 x 4352: 272 tiles of 256 x 256 on 256 CUs.  The first 256 run as
+    whole tiles, the last 16 of the tile order as 128 x 256 halves in a second
+    launch, among them the last, 160-row tile row.  Exact inputs: codes,
+    scales, C and the BF16 output bit for bit against the oracle."""
+    coat = lib()
+    M, N, K = 4000, 4352, 128
+    a, b, sa, sb = inputs.fp8_operands(M, N, K, 7, DEV, "exact")
+    print(f"[gemm] whole rounds + half tiles {M}x{N}x{K} G={G}", flush=True)
+    ref = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(), sa, sb, G, want_c=True)
+    codes, scales, c64, c32 = ref
+    assert np.all(c64 == c32)
+    _assert_bit_exact(f"whole + half G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
+    if G == 128:
+        c = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
+        coat.gemm_bf16(a, b, sa, sb, c)
+        torch.cuda.synchronize()
+        want = torch.from_numpy(c32).to(torch.bfloat16).view(torch.int16).numpy()   # RNE
+        assert np.array_equal(c.cpu().numpy(), want)
+
+
 def test_bad_arguments_rejected_nothing_written():
     coat = lib()
     a, b, sa, sb = inputs.fp8_operands(64, 128, 256, 6, DEV, "exact")

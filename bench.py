@@ -367,14 +367,12 @@ def cpu_baseline_gemm(a, b, sa, sb, G, min_seconds=10.0):
 
 
 def gemm_tiling(M, N):
-    """The library's tile plan for an M x N output: 128 x 128 tiles unless N
-    is a multiple of 256; then 256 x 256 tiles, with the tiles of a last round
-    that would leave over half the CUs idle run as 128 x 256 halves in a
-    second launch."""
+    """The library's tile plan for an M x N output: 256 x 256 tiles (the last
+    tile column 128 wide when N is an odd multiple of 128), with the tiles of
+    a last round that would leave over half the CUs idle run as 128 x 256
+    halves in a second launch."""
     import torch
-    if N % 256:
-        return "128x128"
-    tiles = -(-M // 256) * (N // 256)
+    tiles = -(-M // 256) * -(-N // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rem = tiles % cus
     if rem == 0 or 2 * rem > cus:
@@ -481,8 +479,8 @@ def bench_gemm(args):
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": (f"gemm_fp8_kernel_256<{G}, group quant> (with its half-tile launch, if any: "
-                       f"times are per library call)" if N % 256 == 0 else f"gemm_fp8_kernel<{G}, group quant>"),
+            "kernel": f"gemm_fp8_kernel<{G}, group quant> (with its half-tile launch, if any: "
+                      f"times are per library call)",
             "flops_per_launch": flops,
             "avg_launch_ms": round(ms_launch, 5),
         },

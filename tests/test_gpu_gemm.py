@@ -63,7 +63,7 @@ def _assert_bit_exact(tag, gpu, ref):
         assert np.array_equal(g32.view(np.uint32), r32.view(np.uint32)), f"{tag}: C differs"
 
 
-# N % 256 == 0 takes the 256 x 256 tile kernel, N % 256 == 128 the 128 x 128 one
+# N % 256 == 128 ends in a 128-wide tile column; at most 128 tiles run as 128 x 256 halves
 EXACT_SHAPES = [(1, 128, 128), (100, 256, 256), (128, 128, 512), (257, 384, 128),
                 (64, 1024, 1024), (5, 128, 0), (300, 512, 384), (17, 768, 128), (5, 256, 0)]
 
@@ -80,7 +80,7 @@ def test_exact_inputs_bit_exact(G, shape):
     _assert_bit_exact(f"exact {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
 
 
-# one shape per kernel: N = 384 takes the 128 x 128 tiles, N = 512 the 256 x 256 ones
+# N = 384 ends in a 128-wide tile column, N = 512 does not
 SCALE_SHAPES = [(100, 384, 256), (96, 512, 512)]
 
 

@@ -304,6 +304,42 @@ def test_whole_rounds_and_half_tiles(G):
         assert np.array_equal(c.cpu().numpy(), want)
 
 
+def test_graph_capture_replays_match_eager():
+    """The layer captured in a HIP graph at a shape that takes both launches
+    (4000 x 4352: 256 whole tiles, then 32 half tiles) and replayed three
+    times, with the outputs reset and eager work between replays: every
+    replay's codes, scales and BF16 output equal an eager call's bit for bit."""
+    coat = lib()
+    M, N, K, G = 4000, 4352, 256, 64
+    a, b, sa, sb = inputs.fp8_operands(M, N, K, 9, DEV, "llm")
+    def outs():
+        return (torch.empty((M, N), dtype=torch.uint8, device=DEV),
+                torch.empty((M, N // G), dtype=torch.float32, device=DEV),
+                torch.empty((M, N), dtype=torch.int16, device=DEV))
+    ce, se, be = outs()
+    coat.gemm_group_quant(a, b, sa, sb, ce, se, group_size=G)
+    coat.gemm_bf16(a, b, sa, sb, be)
+    cg, sg, bg = outs()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        coat.gemm_group_quant(a, b, sa, sb, cg, sg, group_size=G)
+        coat.gemm_bf16(a, b, sa, sb, bg)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        cg.fill_(SENTINEL)
+        sg.fill_(float("nan"))
+        bg.fill_(-1)
+        scratch = torch.randn(1 << 16, device=DEV).sum()      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cg, ce), f"replay {replay}: codes"
+        assert torch.equal(sg.view(torch.int32), se.view(torch.int32)), f"replay {replay}: scales"
+        assert torch.equal(bg, be), f"replay {replay}: bf16"
+        del scratch
+
+
 def test_bad_arguments_rejected_nothing_written():
     coat = lib()
     a, b, sa, sb = inputs.fp8_operands(64, 128, 256, 6, DEV, "exact")

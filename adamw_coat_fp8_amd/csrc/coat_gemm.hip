@@ -390,8 +390,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int g = (32 * j + 8 * q) / G;
-          amax[i][g] = fmaxf(fmaxf(amax[i][g], fmaxf(fabsf(acc[i][j][4 * q]), fabsf(acc[i][j][4 * q + 1]))),
-                             fmaxf(fabsf(acc[i][j][4 * q + 2]), fabsf(acc[i][j][4 * q + 3])));
+          // two three-input maxima per four values (v_max3 with |.| modifiers)
+          amax[i][g] = fmaxf(fmaxf(amax[i][g], fabsf(acc[i][j][4 * q])), fabsf(acc[i][j][4 * q + 1]));
+          amax[i][g] = fmaxf(fmaxf(amax[i][g], fabsf(acc[i][j][4 * q + 2])), fabsf(acc[i][j][4 * q + 3]));
         }
     // Per group: the stored scale max / 448 and the multiplier m with
     // code = RNE(c * m), m = fl(s * fl(448 / max)).  Groups whose max lies

@@ -231,8 +231,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
     const uint4 hi = *reinterpret_cast<const uint4*>(panel + panel_off(row, c0 + 1));
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   };
-  // A K step is four MFMA groups g = (kk, h): both row tiles against column
-  // tiles 2h, 2h + 1 at k half kk.  The fragments of group g + 1 are read
+  // A K step is four MFMA groups g = (kk, h): the wave's kI row tiles against
+  // column tiles 2h, 2h + 1 at k half kk.  The fragments of group g + 1 are read
   // while the MFMAs of group g run (two register sets fb0 / fb1 for B, one A
   // set per kk), so the waits on LDS reads are partial.
   v8i fa0[kI], fa1[kI], fb0[2], fb1[2];

@@ -430,7 +430,7 @@ def bench_gemm(args):
                "unfused_bf16_gemm_then_quantizer_ms": round(ms_unfused, 5),
                "fused_saving_vs_unfused": round(1.0 - ms_launch / ms_unfused, 4),
                "tile": gemm_tiling(M, N)}
-    # a library FP8 GEMM (hipBLASLt through torch) for context, if this build has one
+    # a library FP8 GEMM (hipBLASLt through torch) for context, where torch provides one
     try:
         af = a.view(torch.float8_e4m3fn)
         bf = b.view(torch.float8_e4m3fn)
@@ -494,7 +494,7 @@ def bench_gemm(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the step is shard-local and would run unchanged on each GPU's shard.",
               file=sys.stderr)
         sys.exit(2)

@@ -150,21 +150,32 @@ def cpu_baseline(specs, G, hp, sample_params, min_seconds=10.0):
         w, g1, g2, m, v = item
         oracle.adamw_fp8_step(w, g1 if step == 1 else g2, m, v, G, **hp, step=step)
 
-    steps = 0
+    def timed(items, nthreads, seconds):
+        steps = 0
+        with cf.ThreadPoolExecutor(nthreads) as ex:
+            t0 = time.perf_counter()
+            while True:
+                list(ex.map(lambda it: run(it, 2 + steps), items))
+                steps += 1
+                dt = time.perf_counter() - t0
+                if dt >= seconds:
+                    return steps, dt
+
     with cf.ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda it: run(it, 1), work))
-        t0 = time.perf_counter()
-        while True:
-            list(ex.map(lambda it: run(it, 2 + steps), work))
-            steps += 1
-            dt = time.perf_counter() - t0
-            if dt >= min_seconds:
-                break
+    steps, dt = timed(work, threads, min_seconds)
     n_total = sum(n for _, n in pieces)
+    # the same oracle on one host thread, over the first few slices of the sample
+    one = work[:4]
+    n_one = sum(it[0].size for it in one)
+    steps1, dt1 = timed(one, 1, min_seconds / 2)
     return {"value": steps * n_total / dt / 1e9, "unit": "Gparam/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n_total} params: first <=2M elements of the first {len(pieces)} "
-                      f"tensors, {steps} whole steps after one untimed step, {dt:.2f} s wall"}
+                      f"tensors, {steps} whole steps after one untimed step, {dt:.2f} s wall",
+            "single_core": {"value": steps1 * n_one / dt1 / 1e9, "unit": "Gparam/s", "cores": 1,
+                            "sample": f"{n_one} params (the first {len(one)} slices), "
+                                      f"{steps1} whole steps, {dt1:.2f} s wall"}}
 
 
 def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):

@@ -267,6 +267,28 @@ def test_full_size_sampled_rows():
     _interval_check("full llm", a, b, sa, sb, G, (gc[sel], gs[sel], None), rows=sel)
 
 
+# the other Llama-2-7B linear-layer shapes the benchmark is run at: FFN down,
+# fused gate + up, fused QKV, attention output, and a single round of tiles
+LLAMA_SHAPES = [(8192, 4096, 11008), (8192, 22016, 4096), (8192, 12288, 4096),
+                (8192, 4096, 4096), (4096, 4096, 4096)]
+
+
+@pytest.mark.parametrize("shape", LLAMA_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in LLAMA_SHAPES])
+def test_llama_shapes_sampled_rows(shape):
+    """Exact inputs at each shape, G = 128, in the benchmark's launch: six
+    sampled rows (the first and last among them) bit for bit."""
+    M, N, K = shape
+    G = 128
+    rng = np.random.default_rng(M + N + K)
+    print(f"[gemm] sampled rows {M}x{N}x{K}", flush=True)
+    a, b, sa, sb = inputs.fp8_operands(M, N, K, 8, DEV, "exact")
+    gc, gs, _ = _run(a, b, sa, sb, G, want_c=False)
+    sel = np.sort(rng.choice(M, 6, replace=False))
+    sel[0], sel[-1] = 0, M - 1
+    codes, scales = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(), sa, sb, G)
+    _assert_bit_exact(f"sampled {shape}", (gc[sel], gs[sel], None), (codes, scales, None))
+
+
 @pytest.mark.parametrize("shape", [(1, 128, 128), (257, 384, 256), (128, 1024, 1024),
                                    (300, 512, 256)])
 def test_bf16_epilogue(shape):

@@ -214,3 +214,35 @@ def test_free_running_drift_report():
           f"p99.9 {np.quantile(rel, 0.999):.2e}; identical codes m {same_m:.5f} v {same_v:.5f}",
           flush=True)
     assert np.median(rel) < 2e-2 and same_v > 0.99
+
+
+def test_training_trajectory_tracks_fp32_adamw():
+    """The fused step as an optimizer: 400 steps on a small least-squares
+    problem from w = 0, each on the gradient of the GPU's own weights
+    (computed on the host, rounded to BF16).  The weights must stay within 20%
+    of torch.optim.AdamW's FP32-moment run, relative to the distance that run
+    has moved -- the bar the oracle meets with expansion (about 10%) and
+    misses by far without it -- and the loss must follow the FP32 run's."""
+    from toy_problem import LeastSquares, one_torch_thread, relative_deviation, torch_adamw_trajectory
+    coat = lib()
+    steps, G = 400, 128
+    prob = LeastSquares()
+    ref = torch_adamw_trajectory(prob, steps, HP)
+    w = torch.zeros(prob.d, dtype=torch.float32, device=DEV)
+    m = coat.QuantState.zeros(prob.d, G, DEV)
+    v = coat.QuantState.zeros(prob.d, G, DEV)
+    slot = coat.TensorList([coat.ParamSlot(w, torch.zeros(prob.d, dtype=torch.bfloat16, device=DEV), m, v)])
+    traj = []
+    with one_torch_thread():
+        for t in range(1, steps + 1):
+            wh = w.cpu().numpy()
+            slot.slots[0].grad.copy_(prob.grad_bf16(wh).to(DEV))
+            coat.adamw_fp8_step(slot, **HP, step=t, group_size=G)
+            traj.append(w.cpu().numpy().copy())
+    traj = np.array(traj)
+    dev = relative_deviation(traj, ref)
+    print(f"[trajectory] GPU: max relative deviation from FP32 AdamW {dev.max():.3f}", flush=True)
+    assert dev.max() < 0.2
+    for s in (10, 50, 100):
+        want, got = prob.loss(ref[s - 1]), prob.loss(traj[s - 1])
+        assert abs(got - want) <= 0.2 * want, (s, got, want)

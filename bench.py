@@ -22,7 +22,10 @@ on the host cores.
 step quantizes a (tokens x channels) BF16 matrix (default 8192 x 11008: four
 2048-token sequences at the Llama-2-7B FFN width) into E4M3 codes, per-group
 scales and the transposed codes; it reports Gelem/s and the same roofline and
-CPU-oracle objects.
+CPU-oracle objects.  ``--path gemm_group_quant`` measures the group-scaled FP8
+linear layer (TFLOP/s against the matrix cores' FP8 peak), and ``--path codec``
+the stand-alone expand-quantize / dequantize-expand entry points on a
+Llama-2-7B-sized FP32 moment.
 """
 from __future__ import annotations
 
@@ -41,6 +44,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_adamw_fp8_step_llama2_7b.txt")
 PMC_SUMMARY_ACT = os.path.join(ROOT, "profiles", "pmc_quantize_act_8192x11008.txt")
 PMC_SUMMARY_GEMM = os.path.join(ROOT, "profiles", "pmc_gemm_group_quant_8192x11008x4096.txt")
+PMC_SUMMARY_CODEC = os.path.join(ROOT, "profiles", "pmc_codec_llama2_7b.txt")
 _CSRC = os.path.join(ROOT, "adamw_coat_fp8_amd", "csrc")
 # the sources each profiled kernel is built from
 STEP_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_fp8.hip", "coat_common.h")]
@@ -51,7 +55,7 @@ GEMM_SOURCES = [os.path.join(_CSRC, f) for f in ("coat_gemm.hip", "coat_common.h
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--path", choices=("adamw_step", "act_quant", "gemm_group_quant"),
+    ap.add_argument("--path", choices=("adamw_step", "act_quant", "gemm_group_quant", "codec"),
                     default="adamw_step")
     ap.add_argument("--gemm-shape", default="8192x11008x4096",
                     help="M x N x K of the FP8 linear layer (gemm_group_quant)")
@@ -73,10 +77,11 @@ def parse():
     args = ap.parse_args()
     act = args.path == "act_quant"
     gemm = args.path == "gemm_group_quant"
+    codec = args.path == "codec"
     if args.steps is None:
-        args.steps = 200 if act else (100 if gemm else 20)
+        args.steps = 200 if act else (100 if gemm else (10 if codec else 20))
     if args.warmup is None:
-        args.warmup = 20 if act else (30 if gemm else 5)
+        args.warmup = 20 if act else (30 if gemm else (2 if codec else 5))
     return args
 
 
@@ -99,9 +104,11 @@ def act_bytes(rows: int, cols: int, G: int, transpose: bool = True) -> int:
     return rows * cols * (3 + (1 if transpose else 0)) + 4 * rows * (cols // G)
 
 
-def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY, sources=STEP_SOURCES):
-    """HBM traffic per launch from the committed rocprofv3 PMC summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY, sources=STEP_SOURCES,
+                         key="hbm_bytes_per_launch"):
+    """HBM traffic per launch (the summary's `key`) from the committed
+    rocprofv3 PMC summary, if it was taken on the current kernel source; else
+    None."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -112,7 +119,7 @@ def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY, sources=STEP_SOURC
     if kv.get("kernel_source_sha") != kernel_source_sha(sources):
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[key])
     except (KeyError, ValueError):
         return None
 
@@ -502,6 +509,151 @@ def bench_gemm(args):
     print(json.dumps(rec), flush=True)
 
 
+def codec_bytes(n: int, G: int) -> int:
+    """Either direction: FP32 values (4 B) one way, E4M3 codes (1 B) the
+    other, and the group's FP32 scale and k (8 B per group)."""
+    return 5 * n + 8 * ((n + G - 1) // G)
+
+
+def cpu_baseline_codec(G, sample, min_seconds=10.0):
+    """The oracle's expand-quantize and dequantize-expand round trip on a
+    bounded sample, split over host threads in group-aligned slices."""
+    import numpy as np
+    import oracle
+    import torch
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    gen = torch.Generator().manual_seed(7)
+    x = (torch.randn(sample, generator=gen) * 1e-3).numpy()
+    per = -(-sample // threads)
+    per += (-per) % G
+    slices = [x[i:i + per] for i in range(0, sample, per)]
+
+    def run(xs):
+        oracle.dequantize_expand(oracle.expand_quantize(xs, G), G)
+
+    passes = 0
+    with cf.ThreadPoolExecutor(threads) as ex:
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(run, slices))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"value": passes * sample / dt / 1e9, "unit": "Gelem/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{sample} N(0, 1e-3) FP32 values, {passes} round trips "
+                      f"(expand-quantize, then dequantize-expand), {dt:.2f} s wall"}
+
+
+def bench_codec(args):
+    """The stand-alone codec entry points on a Llama-2-7B-sized first moment:
+    expand-quantize of the whole FP32 state into E4M3 codes + scale + k
+    (converting an FP32 optimizer checkpoint), then dequantize-expand back to
+    FP32.  One call each over the flat buffer: every tensor of the workload is
+    a multiple of G elements, so its groups are the per-tensor groups."""
+    import torch
+    from adamw_coat_fp8_amd import coat, inputs
+
+    G = args.group_size
+    specs = inputs.workload_specs(args.workload)
+    numels = [s.numel for s in specs]
+    n = sum(numels)
+    if any(x % G for x in numels):
+        raise SystemExit("codec bench: every tensor must be a multiple of G")
+    print(f"[bench] codec {args.workload}: {n} elements, G={G}", file=sys.stderr, flush=True)
+    torch.cuda.init()
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    stds = inputs.grad_stds(len(specs))
+    off = 0
+    for i, (ne, sd) in enumerate(zip(numels, stds)):   # a first moment ~ (1 - b1) g per tensor
+        x[off:off + ne].normal_(0.0, 0.1 * sd, generator=inputs.generator("cuda", 1000 + i))
+        off += ne
+    state = coat.QuantState.zeros(n, G, "cuda")
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        coat.expand_quantize(x, state, group_size=G, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        coat.dequantize_expand(state, y, group_size=G, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.warmup} warm-up round trips done", file=sys.stderr, flush=True)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    d_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    nbytes = codec_bytes(n, G)
+    q_gbs = nbytes / (q_ms * 1e-3) / 1e9
+    d_gbs = nbytes / (d_ms * 1e-3) / 1e9
+    print(f"[bench] {args.steps} timed round trips: {ms_per_step:.3f} ms wall; expand-quantize "
+          f"{q_ms:.3f} ms ({q_gbs:.0f} GB/s), dequantize-expand {d_ms:.3f} ms ({d_gbs:.0f} GB/s)",
+          file=sys.stderr, flush=True)
+    if args.copy_probe:
+        copy_probe()
+    ceiling = copy_ceiling_gbps()
+    rec = {
+        "metric": "Gelem/s per expand-quantize + dequantize-expand round trip of an FP32 "
+                  "optimizer state + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": round(n / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload} first moment: {n} FP32 values (per-tensor N(0, 0.1 sigma_i)) "
+                        f"<-> E4M3 codes + per-group FP32 scale and k",
+            "group_size": G,
+            "algorithmic_bytes_per_launch": nbytes,
+            "dequantize_expand": {
+                "avg_launch_ms": round(d_ms, 4),
+                "achieved_GBps": round(d_gbs, 1),
+                "frac": round(d_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic_from_profile(nbytes, PMC_SUMMARY_CODEC, STEP_SOURCES,
+                                                "dequantize_hbm_bytes_per_launch"),
+            },
+            "copy_ceiling_GBps": round(ceiling, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(q_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(q_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(nbytes, PMC_SUMMARY_CODEC, STEP_SOURCES,
+                                            "quantize_hbm_bytes_per_launch"),
+            "kernel": f"codec_kernel<{G}, quantize>",
+            "bytes_per_launch": nbytes,
+            "avg_launch_ms": round(q_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline_codec(G, 1 << 26)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -513,6 +665,8 @@ def main():
         return bench_act(args)
     if args.path == "gemm_group_quant":
         return bench_gemm(args)
+    if args.path == "codec":
+        return bench_codec(args)
     import torch
     from adamw_coat_fp8_amd import coat, inputs
     from adamw_coat_fp8_amd.shard import FP8AdamWShard

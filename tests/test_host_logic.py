@@ -127,3 +127,11 @@ def test_activation_recipe_features():
         assert ((tie == tie.round()) & (amax > 0)).any()        # max = 448 * 2^e
     with pytest.raises(ValueError):
         inputs.activation(4, 100, 0, "cpu", "llm", 16)
+
+
+def test_bench_codec_byte_accounting():
+    """Codec traffic: 4 B of FP32 and 1 B of code per element, scale and k
+    (8 B) per group, in either direction."""
+    import bench
+    assert bench.codec_bytes(128 * 1024, 128) == 5 * 128 * 1024 + 8 * 1024
+    assert bench.codec_bytes(1000, 16) == 5 * 1000 + 8 * 63

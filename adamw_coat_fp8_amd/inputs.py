@@ -190,6 +190,16 @@ def fill_weights(shard, seed: int = 0):
         shard.w[e].copy_(weights(shard.numels[i], i, shard.w.device, seed=seed))
 
 
+def fill_moment_like(x: torch.Tensor, numels: Sequence[int], stds: Sequence[float]):
+    """An FP32 first-moment-like state in one flat buffer: tensor i's slice is
+    N(0, 0.1 * stds[i]) (the size of (1 - beta1) g), seed 1000 + i."""
+    off = 0
+    for i, (n, sd) in enumerate(zip(numels, stds)):
+        x[off:off + n].normal_(0.0, 0.1 * sd, generator=generator(x.device, 1000 + i))
+        off += n
+    return x
+
+
 def fill_gradients(shard, step: int, stds: Sequence[float], kind: str = "gaussian"):
     for i in range(len(shard.numels)):
         e = shard.element_range(i)

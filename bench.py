@@ -564,12 +564,8 @@ def bench_codec(args):
         raise SystemExit("codec bench: every tensor must be a multiple of G")
     print(f"[bench] codec {args.workload}: {n} elements, G={G}", file=sys.stderr, flush=True)
     torch.cuda.init()
-    x = torch.empty(n, dtype=torch.float32, device="cuda")
-    stds = inputs.grad_stds(len(specs))
-    off = 0
-    for i, (ne, sd) in enumerate(zip(numels, stds)):   # a first moment ~ (1 - b1) g per tensor
-        x[off:off + ne].normal_(0.0, 0.1 * sd, generator=inputs.generator("cuda", 1000 + i))
-        off += ne
+    x = inputs.fill_moment_like(torch.empty(n, dtype=torch.float32, device="cuda"), numels,
+                                inputs.grad_stds(len(specs)))
     state = coat.QuantState.zeros(n, G, "cuda")
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()

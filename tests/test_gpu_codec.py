@@ -156,3 +156,52 @@ def test_expand_quantize_matches_oracle(G, n):
     nz = ref.scale > 0
     assert np.all(np.abs(gk[nz] - ref.k[nz]) <= 1e-5 * ref.k[nz])
     assert np.all(gk[~nz] == 1.0)
+
+
+def test_full_size_codec_sampled_groups():
+    """Both codec entry points at the benchmark's launch: one call each over a
+    Llama-2-7B-sized FP32 first moment (6,738,415,616 values, G = 128, the
+    benchmark's input recipe).  On 1,500 sampled groups (the first, the one
+    holding element 2^31, the last, and random ones): expand-quantize against
+    the oracle's (scale exact, k within 1e-5, codes by the parity rules), and
+    dequantize-expand of the GPU's own state against the oracle's
+    dequantization of it (within the relative error bound)."""
+    from adamw_coat_fp8_amd import inputs
+    coat = lib()
+    G = 128
+    numels = [s.numel for s in inputs.workload_specs("llama2_7b")]
+    n = sum(numels)
+    ng = n // G
+    print(f"[codec] full size: {n} values", flush=True)
+    x = inputs.fill_moment_like(torch.empty(n, dtype=torch.float32, device=DEV), numels,
+                                inputs.grad_stds(len(numels)))
+    st = coat.QuantState.zeros(n, G, DEV)
+    coat.expand_quantize(x, st, G)
+    y = torch.empty_like(x)
+    coat.dequantize_expand(st, y, G)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    pick = np.array(sorted({0, (1 << 31) // G, ng - 1} | set(int(v) for v in rng.integers(0, ng, 1497))))
+    e = torch.from_numpy((pick[:, None] * G + np.arange(G)[None, :]).ravel()).to(DEV)
+    gsel = torch.from_numpy(pick).to(DEV)
+    xs = x[e].cpu().numpy()
+    ref = oracle.expand_quantize(xs, G)
+    gs, gk = st.scale[gsel].cpu().numpy(), st.k[gsel].cpu().numpy()
+    assert np.array_equal(gs, ref.scale)
+    rep = {}
+    _check_state("x", st.codes[e].cpu().numpy(), gs, gk, ref, xs, np.zeros(xs.size),
+                 np.zeros(xs.size), G, rep, signed=True)
+    nz = ref.scale > 0
+    assert np.all(np.abs(gk[nz] - ref.k[nz]) <= 1e-5 * ref.k[nz])
+    # dequantize-expand of the GPU's own state on the same groups
+    gst = oracle.QuantizedState(st.codes[e].cpu().numpy(), gs.copy(), gk.copy())
+    dref = oracle.dequantize_expand(gst, G).astype(np.float64)
+    got = y[e].cpu().numpy().astype(np.float64)
+    zero = dref == 0
+    assert np.array_equal(got[zero], dref[zero])
+    rel = np.abs(got[~zero] - dref[~zero]) / np.abs(dref[~zero])
+    assert np.all(rel <= dequant_bound(gst, G)[~zero])
+    print(f"[codec] full size: {rep['x']['identical']:.6f} codes identical, dequant max rel err "
+          f"{rel.max(initial=0):.2e}", flush=True)
+    del x, y, st
+    torch.cuda.empty_cache()

@@ -351,21 +351,27 @@ struct LaneData {
 };
 
 // Which elements a lane owns.  A group of G elements belongs to G/16
-// neighbouring lanes; inside the group the lanes interleave in runs of 4
-// elements: lane li of the group owns runs q = 0..3 at
-//   group_start + q * G/4 + 4 * li + (0..3),
-// so one memory instruction (fixed q) has each group's lanes covering G/4
-// consecutive elements: a w access is then G bytes of whole cache lines per
-// group, not one 16-byte piece per 64-byte segment.  Register j = 4q + r.
+// neighbouring lanes.  The lanes of each block of B elements (B = G, except
+// B = 16 for G = 32) interleave in runs of 4: lane lb of the block owns runs
+// q = 0..3 at
+//   block_start + q * B/4 + 4 * lb + (0..3),
+// so one memory instruction (fixed q) has each block's lanes covering B/4
+// consecutive elements: at B = 128 a w access is whole cache lines, not one
+// 16-byte piece per 64-byte segment.  Measured on the 7B-shaped shard, B = 32
+// (2 lanes, 32-byte pieces) streams 11% slower than B = 128 and 8% slower
+// than B = 16 (each lane's 16 elements contiguous), whatever G, so G = 32
+// takes B = 16.  Register j = 4q + r.
 template <int G>
 struct LaneMap {
   static constexpr int kLanesPerGroup = G / kElemsPerLane;
-  static constexpr int kRunStride = G / 4;
+  static constexpr int kBlock = G == 32 ? 16 : G;
+  static constexpr int kLanesPerBlock = kBlock / kElemsPerLane;
+  static constexpr int kRunStride = kBlock / 4;
   int64_t grp;   // group index inside the tensor
   int64_t base;  // element of register 0
   __device__ __forceinline__ LaneMap(int64_t tile_start, int lane) {
     grp = tile_start / G + lane / kLanesPerGroup;
-    base = grp * G + 4 * (lane % kLanesPerGroup);
+    base = tile_start + (int64_t)(lane / kLanesPerBlock) * kBlock + 4 * (lane % kLanesPerBlock);
   }
   __device__ __forceinline__ int64_t run(int q) const { return base + (int64_t)kRunStride * q; }
   __device__ __forceinline__ int64_t elem(int j) const { return run(j >> 2) + (j & 3); }

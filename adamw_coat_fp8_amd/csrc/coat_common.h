@@ -23,6 +23,11 @@ inline bool valid_group_size(int32_t g) { return g == 16 || g == 32 || g == 64 |
 // thread and returns COAT_ERR_HIP.
 __attribute__((visibility("hidden"))) coat_status_t hip_fail(hipError_t e);
 
+// Compute units of the calling thread's current device.  The attribute query
+// costs microseconds, as long as a small kernel, so the count is cached per
+// device after its first query (a constant of the device, not call state).
+__attribute__((visibility("hidden"))) hipError_t current_cu_count(int* cus);
+
 // BF16 values held in the low / high half of a 32-bit word, widened exactly.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

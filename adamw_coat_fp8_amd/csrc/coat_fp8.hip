@@ -26,6 +26,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "coat_common.h"
 
@@ -36,6 +37,31 @@ thread_local char g_last_hip_error[256] = "";
 coat_status_t hip_fail(hipError_t e) {
   snprintf(g_last_hip_error, sizeof(g_last_hip_error), "%s", hipGetErrorString(e));
   return COAT_ERR_HIP;
+}
+
+namespace {
+constexpr int kMaxCachedDevices = 64;
+std::atomic<int> g_cu_count[kMaxCachedDevices];  // 0: not queried yet
+}  // namespace
+
+hipError_t current_cu_count(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxCachedDevices;
+  if (cached) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return hipSuccess;
+    }
+  }
+  int c = 0;
+  e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (cached) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return hipSuccess;
 }
 
 }  // namespace coat

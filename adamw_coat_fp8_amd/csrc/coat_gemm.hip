@@ -521,9 +521,8 @@ hipError_t launch_gemm(GemmParams& p, int32_t group_size, int epi, hipStream_t s
   void* args[] = {&p};
   p.n_tiles = (p.N + kBN - 1) / kBN;
   const int64_t tiles = (p.M + kBM - 1) / kBM * p.n_tiles;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  int cus = 0;
+  hipError_t e = current_cu_count(&cus);
   if (e != hipSuccess) return e;
   const int64_t rem = cus > 0 ? tiles % cus : 0;
   const int64_t whole = rem > 0 && 2 * rem <= cus ? tiles - rem : tiles;

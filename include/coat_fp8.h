@@ -161,8 +161,8 @@ coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x,
  * product rounded to FP32 (groups with max < 2^-100 compute both as if FP32
  * had an unbounded exponent); -0 gives code 0x00, an all-zero group codes 0.
  * cols must be a multiple of group_size.  x, codes and codes_t 16-byte
- * aligned, scales 4-byte aligned; writes into codes_t are 16 bytes wide when
- * rows is a multiple of 16, bytes otherwise.
+ * aligned, scales 4-byte aligned; writes into codes_t are 16, 8 or 4 bytes
+ * wide when rows is a multiple of 16, 8 or 4, bytes otherwise.
  * Errors: NULL_POINTER (x/codes/scales NULL with rows, cols > 0),
  * INVALID_VALUE (rows or cols < 0, cols % group_size != 0, more than 2^31-1
  * tiles of 128 x 128), GROUP_SIZE, MISALIGNED, HIP.

@@ -63,8 +63,9 @@ def _assert_same(tag, gpu, ref):
                                f"{tbad[:4].tolist()}"
 
 
+# rows % 16, 8, 4 select 16-, 8- and 4-byte stores into the transpose (40, 72: 8; 36, 100: 4)
 SHAPES = [(1, 128), (3, 256), (64, 128), (65, 384), (130, 1024), (256, 640), (48, 4096),
-          (17, 1152)]
+          (17, 1152), (40, 1024), (72, 384), (36, 128), (100, 640)]
 
 
 @pytest.mark.parametrize("G", [16, 32, 64, 128])
@@ -105,6 +106,21 @@ def test_without_transpose_same_codes(G):
     assert b[2] is None
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32),
                                                           b[1].view(np.uint32))
+
+
+# Either side of the tile-height switch (128-row tiles at most two per CU on 256 CUs: 64-row
+# tiles), with ragged row counts: 2040 rows (64-row tiles, 8-byte transposed stores), 2180 and
+# 4100 rows (128-row tiles, 4-byte stores), 2179 rows (128-row tiles, byte stores).
+SWITCH_SHAPES = [(2040, 4096), (2180, 4096), (4100, 2048), (2179, 4096)]
+
+
+@pytest.mark.parametrize("shape", SWITCH_SHAPES, ids=[f"{r}x{c}" for r, c in SWITCH_SHAPES])
+def test_tile_height_switch_bit_exact(shape):
+    rows, cols = shape
+    G = 128
+    x = inputs.activation(rows, cols, 5, DEV, "llm", G)
+    print(f"[act] tile switch {rows}x{cols}", flush=True)
+    _assert_same(f"tile switch {rows}x{cols}", _gpu(x, G), _oracle(x, G))
 
 
 def test_full_size_sampled_rows():

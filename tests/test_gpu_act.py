@@ -98,9 +98,11 @@ def test_stress_bit_exact(G, shape):
     _assert_same(f"stress {rows}x{cols} G={G}", _gpu(x, G), ref)
 
 
-@pytest.mark.parametrize("G", [16, 128])
-def test_without_transpose_same_codes(G):
-    x = inputs.activation(96, 512, 4, DEV, "stress", G)
+@pytest.mark.parametrize("G,shape", [(16, (96, 512)), (128, (96, 512)), (64, (4100, 2048))])
+def test_without_transpose_same_codes(G, shape):
+    """The variant without the transposed copy writes the same codes and
+    scales, with 64-row tiles (96 x 512) and 128-row tiles (4100 x 2048)."""
+    x = inputs.activation(*shape, 4, DEV, "stress", G)
     a = _gpu(x, G, transpose=True)
     b = _gpu(x, G, transpose=False)
     assert b[2] is None

@@ -139,13 +139,16 @@ def _need(t: torch.Tensor, name: str, dtypes, min_numel: int):
 def _on_device(**tensors):
     """Every given buffer is HIP device memory (after the type and size checks)."""
     for name, t in tensors.items():
-        if t is not None and t.device.type != "cuda":
+        if t is not None and not t.is_cuda:
             raise ValueError(f"{name} must be a CUDA (HIP device) tensor, not {t.device}")
 
 
 def _stream(stream) -> Optional[int]:
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        # torch's current stream on the current device, as a raw handle: this
+        # query costs about 0.1 us per call, torch.cuda.current_stream() about
+        # 3 us, as long as a small kernel
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)

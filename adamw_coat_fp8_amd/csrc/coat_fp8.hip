@@ -15,9 +15,10 @@
 // of G elements lives in G/16 neighbouring lanes and its max / min reductions
 // are 0..3 DPP steps inside registers (see LaneMap for the interleave that
 // keeps every memory instruction on whole cache lines).  LDS holds only a
-// 2 KB table for dequantization.  Each wave takes one tile, found by a
-// binary search over the launch's tensors, whose descriptors travel in the
-// kernel arguments.
+// 2 KB table for dequantization, filled by each block after its waves have
+// issued their tiles' loads.  Each wave takes one tile, found by a binary
+// search over the launch's tensors, whose descriptors travel in the kernel
+// arguments.
 
 #include <hip/hip_runtime.h>
 
@@ -72,6 +73,12 @@ namespace {
 
 constexpr int kElemsPerLane = 16;
 constexpr int kTileElems = kWave * kElemsPerLane;  // 1024
+// The step kernel's lanes: 16 elements each, as the codec's.  Measured on the
+// 7B-shaped shard, 4 per lane (256 per wave, one 16-byte run of w per lane)
+// streams 12% slower: the per-wave work (tensor lookup, table fill, group
+// constants replicated over 32 lanes) outweighs the finer access pattern.
+constexpr int kStepElems = kElemsPerLane;
+constexpr int kStepTileElems = kWave * kStepElems;
 constexpr int kMaxTensorsPerLaunch = 40;
 
 // [OCP] E4M3: log2 of the largest finite value 448, and log2 of its dynamic
@@ -368,12 +375,13 @@ struct StepParams {
   double exp2_coef[kExp2Terms];  // see exp2_f64
 };
 
-// Registers of one lane: 16 elements.
+// Registers of one lane: E elements.
+template <int E>
 struct LaneData {
-  float w[16];
-  uint32_t g[8];   // BF16 pairs
-  uint32_t mc[4];  // E4M3 codes, 4 per word
-  uint32_t vc[4];
+  float w[E];
+  uint32_t g[E / 2];   // BF16 pairs
+  uint32_t mc[E / 4];  // E4M3 codes, 4 per word
+  uint32_t vc[E / 4];
 };
 
 // Which elements a lane owns.  A group of G elements belongs to G/16
@@ -387,11 +395,12 @@ struct LaneData {
 // (2 lanes, 32-byte pieces) streams 11% slower than B = 128 and 8% slower
 // than B = 16 (each lane's 16 elements contiguous), whatever G, so G = 32
 // takes B = 16.  Register j = 4q + r.
-template <int G>
+template <int G, int E = kElemsPerLane>
 struct LaneMap {
-  static constexpr int kLanesPerGroup = G / kElemsPerLane;
+  static_assert(G / E >= 1 && G / E <= 8, "a group spans 1 to 8 lanes (the DPP reductions)");
+  static constexpr int kLanesPerGroup = G / E;
   static constexpr int kBlock = G == 32 ? 16 : G;
-  static constexpr int kLanesPerBlock = kBlock / kElemsPerLane;
+  static constexpr int kLanesPerBlock = kBlock / E;
   static constexpr int kRunStride = kBlock / 4;
   int64_t grp;   // group index inside the tensor
   int64_t base;  // element of register 0
@@ -410,11 +419,11 @@ constexpr int kExactRounds = 4;
 // set to 0 in mt[] and skipped.  Returns a key >= kEmptyKey if the group has
 // no nonzero value.  `local` is this lane's indexed minimum key (see
 // Stats::add_indexed), `approx` the group's.  Control flow is wave-uniform.
-template <int G>
-__device__ __forceinline__ uint32_t exact_group_min(const LaneData& L, const StepParams& p,
+template <int G, int E>
+__device__ __forceinline__ uint32_t exact_group_min(const LaneData<E>& L, const StepParams& p,
                                                  float sm, float km, uint32_t local,
-                                                 uint32_t approx, float (&mt)[16]) {
-  constexpr int kLanes = LaneMap<G>::kLanesPerGroup;
+                                                 uint32_t approx, float (&mt)[E]) {
+  constexpr int kLanes = LaneMap<G, E>::kLanesPerGroup;
   uint32_t result = 0xFFFFFFFFu;
   bool done = approx >= kEmptyKey;
   uint32_t excluded = 0u;
@@ -425,9 +434,9 @@ __device__ __forceinline__ uint32_t exact_group_min(const LaneData& L, const Ste
       // the element's code byte and BF16 gradient, picked from registers
       uint32_t cw = L.mc[0], gw = L.g[0];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) cw = ((j >> 2) == (uint32_t)q) ? L.mc[q] : cw;
+      for (int q = 1; q < E / 4; ++q) cw = ((j >> 2) == (uint32_t)q) ? L.mc[q] : cw;
 #pragma unroll
-      for (int h = 1; h < 8; ++h) gw = ((j >> 1) == (uint32_t)h) ? L.g[h] : gw;
+      for (int h = 1; h < E / 2; ++h) gw = ((j >> 1) == (uint32_t)h) ? L.g[h] : gw;
       const uint32_t code = (cw >> (8 * (j & 3u))) & 0xFFu;
       const float g = __uint_as_float((j & 1u) ? (gw & 0xFFFF0000u) : (gw << 16));
       const float m = moment_literal(p.b1, dequant_exact(code, sm, km, p.exp2_coef), p.omb1, g);
@@ -448,7 +457,7 @@ __device__ __forceinline__ uint32_t exact_group_min(const LaneData& L, const Ste
     if (!done) {
       uint32_t l2 = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
+      for (int j = 0; j < E; ++j)
         if (!((excluded >> j) & 1u))
           l2 = min(l2, (((__float_as_uint(mt[j]) << 1) - 2u) & 0xFFFFFFF0u) | (uint32_t)j);
       local = l2;
@@ -459,17 +468,17 @@ __device__ __forceinline__ uint32_t exact_group_min(const LaneData& L, const Ste
   if (!done) result = approx & 0xFFFFFFF0u;  // rounds exhausted: FP32 minimum
   if (__builtin_amdgcn_ballot_w64(excluded != 0u) != 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < E; ++j)
       if ((excluded >> j) & 1u) mt[j] = 0.0f;
   }
   return result;
 }
 
-template <int G, bool kFull>
-__device__ __forceinline__ void load_lane(const TensorDesc& T, const LaneMap<G>& map, LaneData& L) {
+template <int G, bool kFull, int E>
+__device__ __forceinline__ void load_lane(const TensorDesc& T, const LaneMap<G, E>& map, LaneData<E>& L) {
   if constexpr (kFull) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < E / 4; ++q) {
       const int64_t e = map.run(q);
       const float4 w = *reinterpret_cast<const float4*>(T.w + e);
       L.w[4 * q] = w.x;
@@ -486,12 +495,12 @@ __device__ __forceinline__ void load_lane(const TensorDesc& T, const LaneMap<G>&
     // Tail tile: element-wise, zero padding past n.  Zeros leave max|x| and
     // the nonzero minimum of a group unchanged.
 #pragma unroll
-    for (int j = 0; j < 16; ++j) L.w[j] = 0.0f;
+    for (int j = 0; j < E; ++j) L.w[j] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) L.g[j] = 0u;
+    for (int j = 0; j < E / 2; ++j) L.g[j] = 0u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { L.mc[j] = 0u; L.vc[j] = 0u; }
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < E / 4; ++j) { L.mc[j] = 0u; L.vc[j] = 0u; }
+    for (int j = 0; j < E; ++j) {
       const int64_t e = map.elem(j);
       if (e < T.n) {
         L.w[j] = T.w[e];
@@ -503,63 +512,72 @@ __device__ __forceinline__ void load_lane(const TensorDesc& T, const LaneMap<G>&
   }
 }
 
-template <int G, bool kFull>
-__device__ __forceinline__ void store_codes(uint8_t* base, const LaneMap<G>& map, int64_t n,
-                                            const uint32_t (&c)[4]) {
+template <int G, bool kFull, int E = kElemsPerLane>
+__device__ __forceinline__ void store_codes(uint8_t* base, const LaneMap<G, E>& map, int64_t n,
+                                            const uint32_t (&c)[E / 4]) {
   if constexpr (kFull) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(base + map.run(q)) = c[q];
+    for (int q = 0; q < E / 4; ++q) *reinterpret_cast<uint32_t*>(base + map.run(q)) = c[q];
   } else {
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < E; ++j) {
       const int64_t e = map.elem(j);
       if (e < n) base[e] = (uint8_t)(c[j >> 2] >> (8 * (j & 3)));
     }
   }
 }
 
-template <int G, bool kFull>
-__device__ __forceinline__ void store_floats(float* base, const LaneMap<G>& map, int64_t n,
-                                             const float (&x)[16]) {
+template <int G, bool kFull, int E = kElemsPerLane>
+__device__ __forceinline__ void store_floats(float* base, const LaneMap<G, E>& map, int64_t n,
+                                             const float (&x)[E]) {
   if constexpr (kFull) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < E / 4; ++q)
       *reinterpret_cast<float4*>(base + map.run(q)) =
           make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
   } else {
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < E; ++j) {
       const int64_t e = map.elem(j);
       if (e < n) base[e] = x[j];
     }
   }
 }
 
-template <int G, bool kFull>
+// One tile of one wave.  kFill: the block's dequantization table is filled
+// here, after this wave's loads are issued and before their first use, so the
+// table's latency and barrier overlap the loads; every wave of the block must
+// then call it, and `have` = false (a wave past the last tile) only fills.
+template <int G, bool kFull, bool kFill>
 __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_start, int lane,
-                                          const StepParams& p, const float2* tab) {
-  constexpr int kLanesPerGroup = LaneMap<G>::kLanesPerGroup;
-  const LaneMap<G> map(tile_start, lane);
+                                          const StepParams& p, float2* tab, bool have) {
+  constexpr int E = kStepElems;
+  constexpr int kLanesPerGroup = LaneMap<G, E>::kLanesPerGroup;
+  const LaneMap<G, E> map(tile_start, lane);
   const int64_t grp = map.grp;
   const int64_t ngroups = (T.n + G - 1) / G;
   const bool grp_ok = kFull || grp < ngroups;
 
   // a1: loads (all issued before any use)
-  LaneData L;
-  load_lane<G, kFull>(T, map, L);
+  LaneData<E> L;
   float sm = 0.0f, km = 0.0f, sv = 0.0f, kv = 0.0f;
-  if (grp_ok) {
-    sm = T.ms[grp];
-    km = T.mk[grp];
-    sv = T.vs[grp];
-    kv = T.vk[grp];
+  if (have) {
+    load_lane<G, kFull>(T, map, L);
+    if (grp_ok) {
+      sm = T.ms[grp];
+      km = T.mk[grp];
+      sv = T.vs[grp];
+      kv = T.vk[grp];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load of the tile in flight together
+  if constexpr (kFill) load_log2_table(tab);
+  if (!have) return;
 
   // a2: dequantize-expand both moments
   const DequantConst dm = dequant_const(sm, km);
   const DequantConst dv = dequant_const(sv, kv);
-  float mt[16], vt[16];
+  float mt[E], vt[E];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < E; ++j) {
     const float2 em = tab[(L.mc[j >> 2] >> (8 * (j & 3))) & 0xFF];
     const float lv = tab[(L.vc[j >> 2] >> (8 * (j & 3))) & 0xFF].x;
     mt[j] = dequant_mag(em.x, dm) * em.y;
@@ -569,7 +587,7 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
   // a3 + a4: moments, bias correction, weight update from unquantized m_t, v_t
   Stats st_m, st_v;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < E; ++j) {
     const float g = (j & 1) ? bf16_hi(L.g[j >> 1]) : bf16_lo(L.g[j >> 1]);
     const float m = moment_literal(p.b1, mt[j], p.omb1, g);
     const float v = fmaf(p.b2, vt[j], p.omb2 * (g * g));
@@ -580,7 +598,7 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
     st_m.add_indexed(m, (uint32_t)j);
     st_v.add(v);
   }
-  store_floats<G, kFull>(T.w, map, T.n, L.w);
+  store_floats<G, kFull, E>(T.w, map, T.n, L.w);
 
   // a5-a7 for the second moment first, so its registers are free for the
   // first moment's exact minimum below.
@@ -588,12 +606,12 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
     const uint32_t v_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_v.max_abs));
     const uint32_t v_min = group_min_u32<kLanesPerGroup>(st_v.min_key);
     const QuantConst qv = quant_const(v_max, v_min);
-    uint32_t ov[4];
+    uint32_t ov[E / 4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < E / 4; ++q)
       ov[q] = pack4(quant_mag(vt[4 * q], qv), quant_mag(vt[4 * q + 1], qv),
                     quant_mag(vt[4 * q + 2], qv), quant_mag(vt[4 * q + 3], qv));
-    store_codes<G, kFull>(T.vc, map, T.n, ov);
+    store_codes<G, kFull, E>(T.vc, map, T.n, ov);
     if ((lane % kLanesPerGroup) == 0 && grp_ok) {
       T.vs[grp] = qv.scale;
       T.vk[grp] = qv.k;
@@ -608,16 +626,16 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
   // (see exact_group_min).
   const uint32_t m_max = group_max_u32<kLanesPerGroup>(__float_as_uint(st_m.max_abs));
   const uint32_t m_min_approx = group_min_u32<kLanesPerGroup>(st_m.min_key);
-  const uint32_t m_min = exact_group_min<G>(L, p, sm, km, st_m.min_key, m_min_approx, mt);
+  const uint32_t m_min = exact_group_min<G, E>(L, p, sm, km, st_m.min_key, m_min_approx, mt);
 
   // a6: expansion exponent and scale (a group whose only nonzero values are
   // exact zeros is empty)
   const QuantConst qm = quant_const(m_min < kEmptyKey ? m_max : 0u, m_min);
 
   // a7: expand, scale, round, pack, store
-  uint32_t om[4];
+  uint32_t om[E / 4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < E / 4; ++q) {
     float a[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -626,7 +644,7 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
     }
     om[q] = pack4(a[0], a[1], a[2], a[3]);
   }
-  store_codes<G, kFull>(T.mc, map, T.n, om);
+  store_codes<G, kFull, E>(T.mc, map, T.n, om);
   if ((lane % kLanesPerGroup) == 0 && grp_ok) {
     T.ms[grp] = qm.scale;
     T.mk[grp] = qm.k;
@@ -638,29 +656,43 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
 // is not a multiple of the tile (tile_end then counts 0 or 1 per tensor).
 // The two are separate kernels so that the rarely used element-wise tail code
 // does not set the register budget, and so the occupancy, of the main one.
+// The launch's tensor holding `tile`: the first whose cumulative tile count
+// exceeds it (entries past the launch's tensors hold INT64_MAX, so the array
+// is monotone); tile_begin is the tensor's first tile.
+__device__ __forceinline__ int find_tensor(const StepParams& p, int64_t tile, int64_t& tile_begin) {
+  int lo = 0, hi = kMaxTensorsPerLaunch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (tile < p.t[mid].tile_end) hi = mid; else lo = mid + 1;
+  }
+  tile_begin = lo > 0 ? p.t[lo - 1].tile_end : 0;
+  return lo;
+}
+
+template <int G, bool kTail, bool kFill>
+__device__ __forceinline__ void step_tile(const StepParams& p, int64_t tile, int lane, float2* tab,
+                                          bool have) {
+  int64_t tile_begin = 0;
+  const TensorDesc& T = p.t[find_tensor(p, have ? tile : 0, tile_begin)];
+  if constexpr (!kTail)
+    step_lane<G, true, kFill>(T, (tile - tile_begin) * kStepTileElems, lane, p, tab, have);
+  else
+    step_lane<G, false, kFill>(T, T.n / kStepTileElems * kStepTileElems, lane, p, tab, have);
+}
+
 template <int G, bool kTail>
 __global__ __launch_bounds__(kBlockThreads) void adamw_fp8_step_kernel(const StepParams p) {
   __shared__ float2 tab[256];
-  load_log2_table(tab);
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave =
       (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
-  for (int64_t tile = wave; tile < p.total_tiles; tile += nwaves) {
-    // first tensor whose cumulative tile count exceeds `tile` (entries past
-    // the launch's tensors hold INT64_MAX, so the array is monotone)
-    int lo = 0, hi = kMaxTensorsPerLaunch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (tile < p.t[mid].tile_end) hi = mid; else lo = mid + 1;
-    }
-    const int64_t tile_begin = lo > 0 ? p.t[lo - 1].tile_end : 0;
-    const TensorDesc& T = p.t[lo];
-    if constexpr (!kTail)
-      step_lane<G, true>(T, (tile - tile_begin) * kTileElems, lane, p, tab);
-    else
-      step_lane<G, false>(T, T.n / kTileElems * kTileElems, lane, p, tab);
-  }
+  // The first tile's loads go out before the table fill (every wave takes
+  // part in the fill, also one without a tile); later tiles, only when the
+  // grid is capped, find the table ready.
+  step_tile<G, kTail, true>(p, wave, lane, tab, wave < p.total_tiles);
+  for (int64_t tile = wave + nwaves; tile < p.total_tiles; tile += nwaves)
+    step_tile<G, kTail, false>(p, tile, lane, tab, true);
 }
 
 // ------------------------------------------- stand-alone quantize kernels
@@ -838,7 +870,7 @@ coat_status_t check_state(const coat_fp8_state_t& s) {
 hipError_t launch_step(StepParams& p, int used, int32_t group_size, hipStream_t stream) {
   int64_t full = 0, tails = 0;
   for (int i = 0; i < used; ++i) {
-    full += p.t[i].n / kTileElems;
+    full += p.t[i].n / kStepTileElems;
     p.t[i].tile_end = full;
   }
   for (int i = used; i < kMaxTensorsPerLaunch; ++i) p.t[i].tile_end = INT64_MAX;
@@ -848,7 +880,7 @@ hipError_t launch_step(StepParams& p, int used, int32_t group_size, hipStream_t 
     if (e != hipSuccess) return e;
   }
   for (int i = 0; i < used; ++i) {
-    tails += (p.t[i].n % kTileElems) ? 1 : 0;
+    tails += (p.t[i].n % kStepTileElems) ? 1 : 0;
     p.t[i].tile_end = tails;
   }
   for (int i = used; i < kMaxTensorsPerLaunch; ++i) p.t[i].tile_end = INT64_MAX;

@@ -137,10 +137,19 @@ def _need(t: torch.Tensor, name: str, dtypes, min_numel: int):
 
 
 def _on_device(**tensors):
-    """Every given buffer is HIP device memory (after the type and size checks)."""
+    """Every given buffer is HIP device memory on the current device, where
+    the library launches its kernels (after the type and size checks)."""
+    dev = None
     for name, t in tensors.items():
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError(f"{name} must be a CUDA (HIP device) tensor, not {t.device}")
+        if dev is None:
+            dev = torch.cuda.current_device()
+        if t.get_device() != dev:
+            raise ValueError(f"{name} is on cuda:{t.get_device()}, but the current device "
+                             f"is cuda:{dev}")
 
 
 def _stream(stream) -> Optional[int]:

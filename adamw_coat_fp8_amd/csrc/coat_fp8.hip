@@ -748,24 +748,32 @@ __device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t tile
   }
 }
 
-template <int G, bool kFull>
+// kFill and have as in step_lane: the block's table is filled after this
+// wave's loads are issued.
+template <int G, bool kFull, bool kFill>
 __device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t tile_start, int lane,
-                                                const float2* tab) {
+                                                float2* tab, bool have) {
   const LaneMap<G> map(tile_start, lane);
   const int64_t grp = map.grp;
-  const bool grp_ok = kFull || grp < (p.n + G - 1) / G;
+  const bool grp_ok = have && (kFull || grp < (p.n + G - 1) / G);
   uint32_t c[4] = {0u, 0u, 0u, 0u};
-  if constexpr (kFull) {
+  if (have) {
+    if constexpr (kFull) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const uint32_t*>(p.codes_in + map.run(q));
-  } else {
-    for (int j = 0; j < 16; ++j) {
-      const int64_t e = map.elem(j);
-      if (e < p.n) c[j >> 2] |= (uint32_t)p.codes_in[e] << (8 * (j & 3));
+      for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const uint32_t*>(p.codes_in + map.run(q));
+    } else {
+      for (int j = 0; j < 16; ++j) {
+        const int64_t e = map.elem(j);
+        if (e < p.n) c[j >> 2] |= (uint32_t)p.codes_in[e] << (8 * (j & 3));
+      }
     }
   }
-  const DequantConst d = dequant_const(grp_ok ? p.scale_in[grp] : 0.0f,
-                                       grp_ok ? p.k_in[grp] : 0.0f);
+  const float s_in = grp_ok ? p.scale_in[grp] : 0.0f;
+  const float k_in = grp_ok ? p.k_in[grp] : 0.0f;
+  __builtin_amdgcn_sched_barrier(0);  // the loads go out before the table fill
+  if constexpr (kFill) load_log2_table(tab);
+  if (!have) return;
+  const DequantConst d = dequant_const(s_in, k_in);
   float x[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -780,18 +788,23 @@ __device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t ti
 template <int G, bool kQuantize, bool kTail>
 __global__ __launch_bounds__(kBlockThreads) void codec_kernel(const CodecParams p) {
   __shared__ float2 tab[256];
-  if constexpr (!kQuantize) load_log2_table(tab);
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave =
       (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * kWavesPerBlock;
   const int64_t tiles = kTail ? 1 : p.n / kTileElems;
-  for (int64_t tile = wave; tile < tiles; tile += nwaves) {
-    const int64_t tile_start = kTail ? p.n / kTileElems * kTileElems : tile * kTileElems;
-    if constexpr (kQuantize)
-      quantize_lane<G, !kTail>(p, tile_start, lane);
-    else
-      dequantize_lane<G, !kTail>(p, tile_start, lane, tab);
+  auto start = [&](int64_t tile) {
+    return kTail ? p.n / kTileElems * kTileElems : tile * kTileElems;
+  };
+  if constexpr (kQuantize) {
+    for (int64_t tile = wave; tile < tiles; tile += nwaves)
+      quantize_lane<G, !kTail>(p, start(tile), lane);
+  } else {
+    // the first tile's loads go out before the table fill, in which every
+    // wave takes part
+    dequantize_lane<G, !kTail, true>(p, start(wave < tiles ? wave : 0), lane, tab, wave < tiles);
+    for (int64_t tile = wave + nwaves; tile < tiles; tile += nwaves)
+      dequantize_lane<G, !kTail, false>(p, start(tile), lane, tab, true);
   }
 }
 

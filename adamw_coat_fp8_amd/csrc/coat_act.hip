@@ -62,9 +62,9 @@ __device__ __forceinline__ uint32_t bf16x8_max_mag(uint4 r) {
   return max(max(a, b), max(c, d));
 }
 
-__device__ __forceinline__ uint32_t act_pack4(uint32_t w0, uint32_t w1, float pre, float r) {
-  const float q0 = scaled_nz(bf16_lo(w0) * pre, r), q1 = scaled_nz(bf16_hi(w0) * pre, r);
-  const float q2 = scaled_nz(bf16_lo(w1) * pre, r), q3 = scaled_nz(bf16_hi(w1) * pre, r);
+__device__ __forceinline__ uint32_t act_pack4(uint32_t w0, uint32_t w1, const GroupQuot& d) {
+  const float q0 = group_quot(bf16_lo(w0), d), q1 = group_quot(bf16_hi(w0), d);
+  const float q2 = group_quot(bf16_lo(w1), d), q3 = group_quot(bf16_hi(w1), d);
   int v = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
   v = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, v, true);
   return (uint32_t)v;
@@ -134,14 +134,11 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_act_kernel(const ActPa
     // row, and cols is a multiple of G
     const uint32_t mag = lanes_max_u32<kLanes>(bf16x8_max_mag(raw[q]));
     const float amax = __uint_as_float(mag << 16);
-    // Below 2^-100, 448 / max would leave FP32's range: scale max and x by 2^64
-    // (exact) so the rounded r and x*r are those of an unbounded exponent.
-    const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
-    const float r = 448.0f / (amax * pre);
+    const GroupQuot d = group_quot_setup(amax);
     const bool nonzero = amax > 0.0f;
     uint2 c;
-    c.x = nonzero ? act_pack4(raw[q].x, raw[q].y, pre, r) : 0u;
-    c.y = nonzero ? act_pack4(raw[q].z, raw[q].w, pre, r) : 0u;
+    c.x = nonzero ? act_pack4(raw[q].x, raw[q].y, d) : 0u;
+    c.y = nonzero ? act_pack4(raw[q].z, raw[q].w, d) : 0u;
     if (ok) {
       store_stream8(p.codes + row * p.cols + col, c);
       if (chunk % kLanes == 0) p.scales[row * p.groups_per_row + col / G] = amax / 448.0f;

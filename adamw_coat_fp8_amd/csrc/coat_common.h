@@ -51,12 +51,43 @@ __device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
   return v;
 }
 
-// x * r rounded once to FP32 (contraction off), with -0 folded to +0: the
-// FP32 product the per-group E4M3 quantizers round, so that only values that
-// round to zero in E4M3 keep a negative sign.
-__device__ __forceinline__ float scaled_nz(float x, float r) {
+// The quotient x / S = 448 x / max of the per-group E4M3 quantizers ([P1]
+// FP8量化, S = max / 448), close enough to the exact one that its E4M3
+// rounding (round to nearest even) is the exact quotient's.  With
+// a = x * (7/8) pre and b = max * pre / 512 (pre = 2^64 for max < 2^-100,
+// else 1; both products exact for x with up to 21 significant bits), a / b
+// is the quotient.  q0 = a * r with r = fl(1/b) is within two ulps of it.
+// When a / b is itself a float -- every E4M3 value and midpoint is one --
+// the residual a - q0 * b = (a/b - q0) * b is exact in one FMA and
+// q1 = q0 + residual * r lands on a / b exactly, so ties are decided as
+// ties.  Otherwise q1 is within about half an ulp of a / b: for BF16 x and
+// max, a / b lies at least 2^-13 (relative) from any midpoint (448 x has 11
+// significant bits, midpoint * max 13), so q1 rounds to the same code; for
+// FP32 x the two can differ only within ~2^-23 of a midpoint.  -0.0 is
+// folded to +0 on a (code 0x00); a negative x whose quotient rounds to zero
+// keeps its sign (0x80).
+struct GroupQuot {
+  float c, b, r;
+};
+
+__device__ __forceinline__ GroupQuot group_quot_setup(float amax) {
+  const float pre = amax < 0x1p-100f ? 0x1p64f : 1.0f;
+  GroupQuot d;
+  d.c = 0.875f * pre;
+  d.b = amax * pre * 0x1p-9f;
+  d.r = 1.0f / d.b;
+  return d;
+}
+
+__device__ __forceinline__ float group_quot(float x, float c, float b, float r) {
 #pragma clang fp contract(off)
-  return x * r + 0.0f;
+  const float a = x * c + 0.0f;
+  const float q0 = a * r;
+  return __builtin_fmaf(__builtin_fmaf(-q0, b, a), r, q0);
+}
+
+__device__ __forceinline__ float group_quot(float x, const GroupQuot& d) {
+  return group_quot(x, d.c, d.b, d.r);
 }
 
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).

@@ -419,6 +419,13 @@ struct LaneMap {
 
 constexpr int kExactRounds = 4;
 
+// Where b1*m and (1-b1)*g cancel, m_t's relative error is the dequantized
+// value's (a few FP32 ulps, up to ~4e-6 for the smallest codes at small k)
+// times |b1*m| / |m_t|, and the expansion multiplies it by k in the code.
+// Below this ratio the product can reach one E4M3 code step (6-12%) even at
+// k = 16, so such elements are re-evaluated exactly (about 1e-3 of them).
+constexpr float kCancelRatio = 0x1p-11f;
+
 // Smallest nonzero |m_t| of the group as a key (2*bits - 2), evaluated
 // exactly for the candidate element; elements found to be exact zeros are
 // set to 0 in mt[] and skipped.  Returns a key >= kEmptyKey if the group has
@@ -589,19 +596,37 @@ __device__ __forceinline__ void step_lane(const TensorDesc& T, int64_t tile_star
     vt[j] = dequant_mag(lv, dv);  // second moment: codes carry no sign
   }
 
-  // a3 + a4: moments, bias correction, weight update from unquantized m_t, v_t
-  Stats st_m, st_v;
+  // a3: moments
+  uint32_t cancel = 0u;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const float g = (j & 1) ? bf16_hi(L.g[j >> 1]) : bf16_lo(L.g[j >> 1]);
     const float m = moment_literal(p.b1, mt[j], p.omb1, g);
-    const float v = fmaf(p.b2, vt[j], p.omb2 * (g * g));
-    const float den = fmaf(hw_sqrt(v), p.den_a, p.den_b);
-    L.w[j] = fmaf(L.w[j], p.decay, -(m * hw_rcp(den)));
+    cancel |= (fabsf(m) < kCancelRatio * fabsf(p.b1 * mt[j])) ? (1u << j) : 0u;
+    vt[j] = fmaf(p.b2, vt[j], p.omb2 * (g * g));
     mt[j] = m;
-    vt[j] = v;
-    st_m.add_indexed(m, (uint32_t)j);
-    st_v.add(v);
+  }
+  // strongly cancelling first moments, exactly (rare: the block is skipped
+  // unless some lane of the wave has one)
+  if (__builtin_amdgcn_ballot_w64(cancel != 0u) != 0) {
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      if ((cancel >> j) & 1u) {
+        const float g = (j & 1) ? bf16_hi(L.g[j >> 1]) : bf16_lo(L.g[j >> 1]);
+        const uint32_t code = (L.mc[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        mt[j] = moment_literal(p.b1, dequant_exact(code, sm, km, p.exp2_coef), p.omb1, g);
+      }
+    }
+  }
+
+  // a4: bias correction, weight update from the unquantized m_t, v_t
+  Stats st_m, st_v;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const float den = fmaf(hw_sqrt(vt[j]), p.den_a, p.den_b);
+    L.w[j] = fmaf(L.w[j], p.decay, -(mt[j] * hw_rcp(den)));
+    st_m.add_indexed(mt[j], (uint32_t)j);
+    st_v.add(vt[j]);
   }
   store_floats<G, kFull, E>(T.w, map, T.n, L.w);
 

@@ -394,11 +394,12 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
           amax[i][g] = fmaxf(fmaxf(amax[i][g], fabsf(acc[i][j][4 * q])), fabsf(acc[i][j][4 * q + 1]));
           amax[i][g] = fmaxf(fmaxf(amax[i][g], fabsf(acc[i][j][4 * q + 2])), fabsf(acc[i][j][4 * q + 3]));
         }
-    // Per group: the stored scale max / 448 and the multiplier m with
-    // code = RNE(c * m), m = fl(s * fl(448 / max)).  Groups whose max lies
-    // outside [2^-100, FLT_MAX] (and zero groups) get m = 0 here and are
-    // handled below.
-    float mul[kI][kGW];
+    // Per group: the stored scale max / 448 and the divisor b = max / 512 with
+    // its reciprocal r, for group_quot on C = fl(c s) (a = C * 7/8, q = a / b).
+    // Groups whose max lies below 2^-100 (or past FP32's range) need the
+    // 2^64 pre-scale; they get b = r = 0 here (all codes 0) and are redone
+    // below.
+    float qb[kI][kGW], qr[kI][kGW];
     bool slow = false;
 #pragma unroll
     for (int i = 0; i < kI; ++i)
@@ -406,7 +407,8 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
       for (int g = 0; g < kGW; ++g) {
         amax[i][g] = scale_acc(pair_max(amax[i][g]), s_abs);
         const bool fast = amax[i][g] >= 0x1p-100f && amax[i][g] <= 0x1.fffffep127f;
-        mul[i][g] = fast ? scale_acc(448.0f / amax[i][g], s) : 0.0f;
+        qb[i][g] = fast ? amax[i][g] * 0x1p-9f : 0.0f;
+        qr[i][g] = fast ? 1.0f / qb[i][g] : 0.0f;
         slow |= !fast && amax[i][g] > 0.0f;
       }
     uint32_t word[kI][4][4];
@@ -416,17 +418,16 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float m = mul[i][(32 * j + 8 * q) / G];
-          // fma(c, m, +0) folds an exact -0 product to +0
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(acc[i][j][4 * q], m, 0.0f),
-                                                  __builtin_fmaf(acc[i][j][4 * q + 1], m, 0.0f), 0, false);
-          w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(acc[i][j][4 * q + 2], m, 0.0f),
-                                              __builtin_fmaf(acc[i][j][4 * q + 3], m, 0.0f), w, true);
+          const int g = (32 * j + 8 * q) / G;
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            x[e] = group_quot(scale_acc(acc[i][j][4 * q + e], s), 0.875f, qb[i][g], qr[i][g]);
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
           word[i][j][q] = (uint32_t)w;
         }
     if (slow) {
-      // Maxima below 2^-100 (448 / max would leave FP32's range: scale by
-      // 2^64) or past FP32's range: round c s first, as the definition does.
 #pragma unroll
       for (int i = 0; i < kI; ++i)
 #pragma unroll
@@ -435,12 +436,12 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
           for (int q = 0; q < 4; ++q) {
             const float am = amax[i][(32 * j + 8 * q) / G];
             if (!(am >= 0x1p-100f && am <= 0x1.fffffep127f) && am > 0.0f) {
-              const float pre = am < 0x1p-100f ? 0x1p64f : 1.0f;
-              const float rq = 448.0f / (am * pre);
-              const float x0 = scale_acc(acc[i][j][4 * q], s), x1 = scale_acc(acc[i][j][4 * q + 1], s);
-              const float x2 = scale_acc(acc[i][j][4 * q + 2], s), x3 = scale_acc(acc[i][j][4 * q + 3], s);
-              int w = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x0 * pre, rq), scaled_nz(x1 * pre, rq), 0, false);
-              w = __builtin_amdgcn_cvt_pk_fp8_f32(scaled_nz(x2 * pre, rq), scaled_nz(x3 * pre, rq), w, true);
+              const GroupQuot d = group_quot_setup(am);
+              float x[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] = group_quot(scale_acc(acc[i][j][4 * q + e], s), d);
+              int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+              w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
               word[i][j][q] = (uint32_t)w;
             }
           }

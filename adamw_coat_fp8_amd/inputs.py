@@ -227,8 +227,10 @@ def activation(rows: int, cols: int, seed: int, device, kind: str = "llm",
     ``stress`` adds, per 1 x group_size group of a row (a uniform draw picks
     the class): 2% all-zero; 2% a single nonzero; 2% magnitudes scaled by
     1e-39 (BF16 subnormals); 2% by 2^-110 (normal, below 2^-100); 2% by 1e30;
-    4% tie groups (one element +-448 * 2^e, the rest +-midpoints between
-    neighbouring E4M3 values times 2^e, e in {-20, -7, 0, 10}); 2% with -0.0 on
+    4% tie groups (one element +-448 * s, the rest +-midpoints between
+    neighbouring E4M3 values times s, with s = 2^e in half of them and
+    s = 0.75 * 2^e, a group max that is not a power of two, in the other half;
+    e in {-20, -7, 0, 10}; all exact in BF16); 2% with -0.0 on
     every other element; 2% wide groups (one element +-1e30, the rest N(0,1)
     times 1e-20 in half of them, whose scaled values underflow FP32, and times
     1e-5 in the other half, which scale to tiny normal FP32 values)."""
@@ -266,7 +268,8 @@ def activation(rows: int, cols: int, seed: int, device, kind: str = "llm",
     x = torch.where((u >= 0.06) & (u < 0.08), x * 2.0 ** -110, x)
     x = torch.where((u >= 0.08) & (u < 0.10), x * 1e30, x)
     tie = (u >= 0.10) & (u < 0.14)
-    x = torch.where(tie, sign * escale * torch.where(lead, 448.0, mid), x)
+    tscale = escale * torch.where(u < 0.12, 1.0, 0.75)
+    x = torch.where(tie, sign * tscale * torch.where(lead, 448.0, mid), x)
     negz = (u >= 0.14) & (u < 0.16) & (within % 2 == 1)
     x = torch.where(negz, torch.full_like(x, -0.0), x)
     wide = (u >= 0.16) & (u < 0.18)

@@ -306,15 +306,17 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
 
 /* --------------------------------------------- activation quantizer (1xG) */
 
-/* [P1] eq. FP8量化 on each 1xG group of a row: S = max|X| / 448 and
- * X_FP8 = round(X / S), evaluated as x * (448 / max) in FP32. */
-/* One 1xG group of FP32 values through [P1] eq. FP8量化 with S = max|x| / 448.
- * Reading: the rounding decisions are taken in FP32, r = 448 / max and
- * q = x * r each rounded to FP32, code = RNE_E4M3(q); the stored scale is
- * S = max / 448 (IEEE division).  An all-zero group stores S = 0 and codes 0.
- * Below 2^-100, 448 / max would overflow FP32's exponent range, so such
- * groups scale max and x by 2^64 first (exact; the rounded results are those
- * of an FP32 with unbounded exponent). */
+/* One 1xG group through [P1] eq. FP8量化: S = max|X| / 448 and
+ * X_FP8 = round(X / S), rounding to nearest with ties to even (reading).
+ * The code is decided on the exact quotient X / S = 448 x / max.  In double,
+ * 448 x is exact (an FP32 x has 24 significant bits) and the one division by
+ * max rounds to 53 bits.  That rounding cannot move the quotient across an
+ * E4M3 midpoint, nor onto one: a midpoint has 5 significant bits, so
+ * 448 x - midpoint * max is either zero or at least 2^-30 of either term,
+ * far above 2^-53.  Hence the double quotient rounds to the same E4M3 value
+ * as the exact one.  The sign is that of x (a negative value that rounds to
+ * zero keeps it: 0x80); -0.0 and zero give 0x00.  The stored scale is S
+ * rounded once to FP32.  An all-zero group stores S = 0 and codes 0. */
 static void quantize_group_e4m3(const float* x, int64_t len, uint8_t* codes, float* scale) {
   float amax = 0.0f;
   for (int64_t j = 0; j < len; ++j) {
@@ -326,13 +328,10 @@ static void quantize_group_e4m3(const float* x, int64_t len, uint8_t* codes, flo
     for (int64_t j = 0; j < len; ++j) codes[j] = 0x00;
     return;
   }
-  const int tiny = amax < 0x1p-100f;
-  const float pre = tiny ? 0x1p64f : 1.0f;
-  const float r = (float)kE4M3Max / (amax * pre);
   *scale = amax / (float)kE4M3Max;
   for (int64_t j = 0; j < len; ++j) {
-    const float q = (x[j] * pre) * r;
-    codes[j] = coat_oracle_e4m3_encode((double)q);
+    const double q = (kE4M3Max * (double)x[j]) / (double)amax;
+    codes[j] = coat_oracle_e4m3_encode(q);
   }
 }
 

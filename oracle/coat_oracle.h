@@ -95,11 +95,12 @@ int coat_oracle_adamw_fp8_step(float* w, const uint16_t* grad_bf16,
 /* Per-group E4M3 quantization of a row-major BF16 activation matrix
  * ([P1] section 三 "混合粒度激活量化": 1xG groups for non-linear layers, and the
  * non-linear-layer kernel's quantized output plus transposed quantized output;
- * [P1] eq. FP8量化 with S = max|X| / 448 per group).  Reading: the rounding
- * decision is taken in FP32, r = 448 / max (IEEE division), code =
- * RNE(x * r); the stored scale is S = max / 448 (IEEE division); an all-zero
- * group stores S = 0 and codes 0.  Groups with max < 2^-100 take r and x*r
- * as an FP32 with unbounded exponent range would (exact 2^64 prescale).  cols must be a multiple of group_size.
+ * [P1] eq. FP8量化 with S = max|X| / 448 per group).  Each code is the E4M3
+ * value nearest to the exact quotient x / S = 448 x / max, ties to even
+ * (reading of the equation's rounding), with the sign of x (a negative value
+ * that rounds to zero gives 0x80; -0.0 gives 0x00); the stored scale is S
+ * rounded once to FP32; an all-zero group stores S = 0 and codes 0.  cols
+ * must be a multiple of group_size.
  * codes: rows x cols, scales: rows x cols/group_size, codes_t: cols x rows
  * (the transpose of codes; may be NULL). */
 int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
@@ -112,7 +113,8 @@ int coat_oracle_quantize_act(const uint16_t* x_bf16, int64_t rows, int64_t cols,
  * A: M x K and B: N x K E4M3 codes, row-major (K contiguous).  Reading: C is
  * the real product (the sum over k is exact in integer arithmetic, the scale
  * is applied in double) rounded to FP32, and its 1xG groups along each row go
- * through the same FP32 quantizer as the activation quantizer above.
+ * through the same quantizer as the activation quantizer above (exact
+ * quotient, ties to even).
  * codes: M x N, scales: M x N/G; c_exact (M x N doubles) and c_f32 (M x N)
  * are optional (NULL to skip).  K <= 2^17; N a multiple of group_size; NaN
  * codes in A or B give COAT_ORACLE_ESTATE. */

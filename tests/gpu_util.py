@@ -1,13 +1,14 @@
 """Helpers shared by the GPU tests: host<->device copies of states and the
 per-step "oracle-forced" check (the GPU starts each step from the oracle's
-state; no oracle input ever comes from the GPU)."""
+state; no oracle input ever comes from the GPU).  The identical-code gate
+applies over every code of the call, per state."""
 from __future__ import annotations
 
 import numpy as np
 import torch
 
 import oracle
-from parity import compare_step, oracle_reference
+from parity import compare_step, gate_identical, oracle_reference
 
 DEV = "cuda"
 
@@ -62,4 +63,5 @@ def forced_step_check(tensors, hp, step, G, reports=None):
                    v_k=s.v.k.cpu().numpy())
         reps.append(compare_step(gpu, ref, G, hp, step))
         out.append(dict(w=ref["w"], m=ref["m"], v=ref["v"]))
+    gate_identical(reps, f"step {step}")
     return out, reps

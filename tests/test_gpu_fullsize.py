@@ -17,7 +17,7 @@ import torch
 import oracle
 from adamw_coat_fp8_amd import inputs
 from gpu_util import DEV, lib, require_gpu
-from parity import compare_step, oracle_reference
+from parity import compare_step, oracle_reference, summary
 
 pytestmark = pytest.mark.gpu
 
@@ -104,12 +104,8 @@ def _run(workload, G, kind, warm, per_tensor, extra_tail=False):
                    v_codes=shard.v_codes[e].cpu().numpy(), v_scale=shard.v_scale[gs].cpu().numpy(),
                    v_k=shard.v_k[gs].cpu().numpy())
         reps.append(compare_step(gpu, ref, G, HP, t))
-    r = reps[0]
-    print(f"[fullsize] {workload} G={G} step {t}: {sum(sizes)} sampled params in "
-          f"{len(sizes)} groups; identical codes m {r['m']['identical']:.6f} "
-          f"v {r['v']['identical']:.6f}; max rel scale {r['m']['max_rel_scale']:.1e}/"
-          f"{r['v']['max_rel_scale']:.1e}; k within 1e-5: m {r['m']['k_groups_within_1e5']:.4f} "
-          f"v {r['v']['k_groups_within_1e5']:.4f}", flush=True)
+    print(f"[fullsize] {summary(reps, f'{workload} G={G} step {t}, {sum(sizes)} sampled params in {len(sizes)} groups')}",
+          flush=True)
     del shard
     return reps
 

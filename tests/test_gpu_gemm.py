@@ -4,7 +4,12 @@ oracle.
 
 Exact inputs (small-integer E4M3 codes, power-of-two scales): every partial
 sum is an integer below 2^24, so the FP32 accumulation is exact in any order
-and C, the codes and the scales must equal the oracle's bit for bit.
+and C and the scales must equal the oracle's bit for bit.  The oracle codes
+each value as the page's quantizer does, RNE of the exact quotient
+448 C / max; the kernel rounds C * fl(448 / max) in FP32, within 2^-23 of it.
+So at least 99.99% of codes must be identical, and every other code must be
+a neighbour of the oracle's across a midpoint that the exact quotient lies
+within 2^-21 (relative) of.
 
 Realistic inputs (per-tensor E4M3 activations with outlier channels and
 N(0, 0.02) weights): the FP8 matrix-core dot product is not an FP32 sum.
@@ -53,14 +58,41 @@ def _run(a, b, sa, sb, G, want_c=True):
             None if c32 is None else c32.cpu().numpy())
 
 
-def _assert_bit_exact(tag, gpu, ref):
+NEAR_TIE = 2.0 ** -21       # relative distance of the exact quotient to a midpoint
+MIN_IDENTICAL_EXACT = 0.9999
+
+
+def assert_codes_near_ties(tag, gc, rc, c, G):
+    """gc, rc: GPU and oracle codes (M x N); c: the exact C (float64) the
+    oracle quantized.  Codes differ only across a midpoint the exact quotient
+    448 C / max nearly sits on, and at most 1e-4 of them."""
+    M, N = rc.shape
+    diff = np.argwhere(gc != rc)
+    frac = 1.0 - len(diff) / max(1, gc.size)
+    assert gc.size < 10_000 and len(diff) <= 1 or frac >= MIN_IDENTICAL_EXACT, \
+        f"{tag}: only {frac:.6f} of codes identical"
+    if len(diff) == 0:
+        return
+    amax = np.abs(c).reshape(M, N // G, G).max(-1)
+    i, j = diff[:, 0], diff[:, 1]
+    q = 448.0 * c[i, j] / amax[i, j // G]
+    og = signed_ordinal(gc[i, j]).astype(np.int64)
+    orf = signed_ordinal(rc[i, j]).astype(np.int64)
+    assert np.all(np.abs(og - orf) == 1), f"{tag}: codes more than one ordinal apart"
+    vg = oracle.e4m3_decode_array(gc[i, j])
+    vr = oracle.e4m3_decode_array(rc[i, j])
+    mid = (vg + vr) / 2
+    assert np.all(np.abs(q - mid) <= NEAR_TIE * np.abs(mid)), \
+        f"{tag}: a code differs away from a midpoint: q {q[:3]} mid {mid[:3]}"
+
+
+def _assert_bit_exact(tag, gpu, ref, G):
     gc, gs, g32 = gpu
     rc, rs, r32 = ref
-    bad = np.argwhere(gc != rc)
-    assert bad.size == 0, f"{tag}: {len(bad)} codes differ, first {bad[:3].tolist()}"
     assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), f"{tag}: scales differ"
     if g32 is not None:
         assert np.array_equal(g32.view(np.uint32), r32.view(np.uint32)), f"{tag}: C differs"
+    assert_codes_near_ties(tag, gc, rc, r32.astype(np.float64), G)
 
 
 # N % 256 == 128 ends in a 128-wide tile column; at most 128 tiles run as 128 x 256 halves
@@ -77,7 +109,7 @@ def test_exact_inputs_bit_exact(G, shape):
     codes, scales, c64, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(),
                                                           sa, sb, G, want_c=True)
     assert np.all(c64 == c32)                       # the inputs keep C exact in FP32
-    _assert_bit_exact(f"exact {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
+    _assert_bit_exact(f"exact {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32), G)
 
 
 # N = 384 ends in a 128-wide tile column, N = 512 does not
@@ -88,12 +120,15 @@ SCALE_SHAPES = [(100, 384, 256), (96, 512, 512)]
 @pytest.mark.parametrize("shape", SCALE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SCALE_SHAPES])
 def test_folded_multiplier_exact_inputs(G, shape):
     """A scale product s that is not a power of two (0.1 * 3.0), on exact
-    integer-valued accumulators c: the scales are fl(max|c| |s|) / 448 and the
-    codes RNE(c * m) with m = fl(s * fl(448 / max)), bit for bit (FP32 steps
-    emulated in numpy, E4M3 rounding by the oracle's encoder).  Against the
-    definition (the oracle, which multiplies by the exact product of the two
-    scales) the scales agree to two FP32 roundings and the codes are at most
-    one E4M3 step away."""
+    integer-valued accumulators c: the library rounds s to FP32, forms
+    C = fl(c s), stores the scales fl(max|C|) / 448 and codes each value by
+    the rounded quotient q1 of the FP32 steps a = C * 7/8, b = max / 512,
+    r = fl(1/b), q0 = fl(a r), q1 = fma(fma(-q0, b, a), r, q0) -- bit for bit
+    (FP32 steps emulated in numpy, each FMA as one rounding of its exact
+    value, E4M3 rounding by the oracle's encoder).  Against the definition
+    (the oracle, which multiplies by the exact product of the two scales) the
+    scales agree to two FP32 roundings and the codes are at most one E4M3
+    step away."""
     M, N, K = shape
     a, b, _, _ = inputs.fp8_operands(M, N, K, 4, DEV, "exact")
     sa, sb = 0.1, 3.0
@@ -104,14 +139,21 @@ def test_folded_multiplier_exact_inputs(G, shape):
     c32 = c.astype(np.float32)
     assert np.all(c32 == c)                          # integer sums below 2^24
     s = np.float32(np.float32(sa) * np.float32(sb))
-    amax = np.abs(c32).reshape(M, N // G, G).max(-1) * np.abs(s)
+    cs = (c32 * s).astype(np.float32)               # fl(c s)
+    amax = np.abs(cs).reshape(M, N // G, G).max(-1)
     assert amax.dtype == np.float32 and np.all((amax == 0) | (amax >= 2.0 ** -100))
     want_s = amax / np.float32(448.0)
     assert np.array_equal(gs.view(np.uint32), want_s.view(np.uint32))
-    with np.errstate(divide="ignore"):
-        m = np.where(amax > 0, s * (np.float32(448.0) / amax), np.float32(0.0)).astype(np.float32)
-    q = c32.reshape(M, N // G, G) * m[..., None] + np.float32(0.0)
-    want_c = oracle.e4m3_encode_array(q.reshape(-1).astype(np.float64)).reshape(M, N)
+    f64 = np.float64
+    with np.errstate(divide="ignore", invalid="ignore"):
+        bq = (amax * np.float32(2.0 ** -9)).astype(np.float32)[..., None]
+        rq = np.where(bq > 0, np.float32(1.0) / bq, np.float32(0.0)).astype(np.float32)
+    aq = (cs.reshape(M, N // G, G) * np.float32(0.875) + np.float32(0.0)).astype(np.float32)
+    q0 = (aq * rq).astype(np.float32)
+    # the exact residual and the correction fit in a double (one rounding each)
+    e = (f64(aq) - f64(q0) * f64(bq)).astype(np.float32)
+    q1 = (f64(e) * f64(rq) + f64(q0)).astype(np.float32)
+    want_c = oracle.e4m3_encode_array(q1.reshape(-1).astype(np.float64)).reshape(M, N)
     bad = np.argwhere(gc != want_c)
     assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}"
     # the oracle multiplies by the exact product of the two scales, the
@@ -128,7 +170,7 @@ def test_folded_multiplier_exact_inputs(G, shape):
 def test_tiny_scale_product(G, shape):
     """s = 2^-120: every group maximum lies below 2^-100, where 448 / max
     leaves FP32's range; those groups are quantized from fl(c s) with the
-    2^64 pre-scale, bit for bit as the oracle does."""
+    2^64 pre-scale: scales and C bit for bit, codes by the near-tie rule."""
     M, N, K = shape
     a, b, _, _ = inputs.fp8_operands(M, N, K, 5, DEV, "exact")
     sa = sb = 2.0 ** -60
@@ -136,7 +178,7 @@ def test_tiny_scale_product(G, shape):
     codes, scales, c64, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(),
                                                           sa, sb, G, want_c=True)
     assert np.all(c64 == c32) and np.max(np.abs(c32)) < 2.0 ** -100
-    _assert_bit_exact(f"tiny scale {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
+    _assert_bit_exact(f"tiny scale {shape} G={G}", _run(a, b, sa, sb, G), (codes, scales, c32), G)
 
 
 def _interval_check(tag, a, b, sa, sb, G, gpu, rows=None):
@@ -252,15 +294,17 @@ def test_matrix_core_dot_product_model():
 def test_full_size_sampled_rows():
     """8192 x 11008 x 4096 (Llama-2-7B FFN up-projection over four 2048-token
     sequences), G = 128, in the launch the benchmark times: exact inputs on 12
-    sampled rows bit for bit, realistic inputs on 6 rows within the bound."""
+    sampled rows (C-derived scales bit for bit, codes by the near-tie rule),
+    realistic inputs on 6 rows within the bound."""
     M, N, K, G = 8192, 11008, 4096, 128
     rng = np.random.default_rng(0)
     a, b, sa, sb = inputs.fp8_operands(M, N, K, 3, DEV, "exact")
     gc, gs, _ = _run(a, b, sa, sb, G, want_c=False)
     sel = np.sort(rng.choice(M, 12, replace=False))
     sel[0], sel[-1] = 0, M - 1
-    codes, scales = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(), sa, sb, G)
-    _assert_bit_exact("full exact", (gc[sel], gs[sel], None), (codes, scales, None))
+    codes, scales, _, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(),
+                                                        sa, sb, G, want_c=True)
+    _assert_bit_exact("full exact", (gc[sel], gs[sel], None), (codes, scales, c32), G)
     a, b, sa, sb = inputs.fp8_operands(M, N, K, 4, DEV, "llm")
     gc, gs, _ = _run(a, b, sa, sb, G, want_c=False)
     sel = np.sort(rng.choice(M, 6, replace=False))
@@ -276,7 +320,8 @@ LLAMA_SHAPES = [(8192, 4096, 11008), (8192, 22016, 4096), (8192, 12288, 4096),
 @pytest.mark.parametrize("shape", LLAMA_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in LLAMA_SHAPES])
 def test_llama_shapes_sampled_rows(shape):
     """Exact inputs at each shape, G = 128, in the benchmark's launch: six
-    sampled rows (the first and last among them) bit for bit."""
+    sampled rows (the first and last among them), scales bit for bit and codes
+    by the near-tie rule."""
     M, N, K = shape
     G = 128
     rng = np.random.default_rng(M + N + K)
@@ -285,8 +330,9 @@ def test_llama_shapes_sampled_rows(shape):
     gc, gs, _ = _run(a, b, sa, sb, G, want_c=False)
     sel = np.sort(rng.choice(M, 6, replace=False))
     sel[0], sel[-1] = 0, M - 1
-    codes, scales = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(), sa, sb, G)
-    _assert_bit_exact(f"sampled {shape}", (gc[sel], gs[sel], None), (codes, scales, None))
+    codes, scales, _, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(),
+                                                        sa, sb, G, want_c=True)
+    _assert_bit_exact(f"sampled {shape}", (gc[sel], gs[sel], None), (codes, scales, c32), G)
 
 
 @pytest.mark.parametrize("shape", [(1, 128, 128), (257, 384, 256), (128, 1024, 1024),
@@ -308,8 +354,9 @@ def test_bf16_epilogue(shape):
 def test_whole_rounds_and_half_tiles(G):
     """4000 x 4352: 272 tiles of 256 x 256 on 256 CUs.  The first 256 run as
     whole tiles, the last 16 of the tile order as 128 x 256 halves in a second
-    launch, among them the last, 160-row tile row.  Exact inputs: codes,
-    scales, C and the BF16 output bit for bit against the oracle."""
+    launch, among them the last, 160-row tile row.  Exact inputs: scales, C
+    and the BF16 output bit for bit against the oracle, codes by the
+    near-tie rule."""
     coat = lib()
     M, N, K = 4000, 4352, 128
     a, b, sa, sb = inputs.fp8_operands(M, N, K, 7, DEV, "exact")
@@ -317,7 +364,7 @@ def test_whole_rounds_and_half_tiles(G):
     ref = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(), sa, sb, G, want_c=True)
     codes, scales, c64, c32 = ref
     assert np.all(c64 == c32)
-    _assert_bit_exact(f"whole + half G={G}", _run(a, b, sa, sb, G), (codes, scales, c32))
+    _assert_bit_exact(f"whole + half G={G}", _run(a, b, sa, sb, G), (codes, scales, c32), G)
     if G == 128:
         c = torch.full((M, N), -1, dtype=torch.int16, device=DEV)
         coat.gemm_bf16(a, b, sa, sb, c)

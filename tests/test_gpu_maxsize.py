@@ -13,7 +13,8 @@ import torch
 import oracle
 from adamw_coat_fp8_amd import inputs
 from gpu_util import DEV, bits_np, lib, require_gpu
-from parity import compare_step, oracle_reference
+from parity import compare_step, oracle_reference, summary
+from test_gpu_gemm import assert_codes_near_ties
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +44,7 @@ def test_step_tensor_past_2_31_elements():
     er = shard.element_range(0)                    # the buffers are padded past n
     shard.w[er] = inputs.weights(n, 0, DEV)
     rng = np.random.default_rng(9)
-    pick = sorted({0, (1 << 31) // G, ng - 2, ng - 1} | set(int(x) for x in rng.integers(0, ng, 12)))
+    pick = sorted({0, (1 << 31) // G, ng - 2, ng - 1} | set(int(x) for x in rng.integers(0, ng, 100)))
     full = [j for j in pick if j < ng - 1]
     pieces = [full, [ng - 1]]                      # full groups together; the tail alone
     eidx, gsel, st = [], [], []
@@ -67,6 +68,7 @@ def test_step_tensor_past_2_31_elements():
     shard.grad[er] = inputs.gradient(n, 1e-3, 3, 0, DEV)
     shard.step(3, **HP)
     torch.cuda.synchronize()
+    reps = []
     for s, e, gs in zip(st, eidx, gsel):
         g = shard.grad[e].view(torch.int16).cpu().numpy().view(np.uint16)
         ref = oracle_reference(s["w"], g, s["m"], s["v"], G, HP, 3)
@@ -74,7 +76,8 @@ def test_step_tensor_past_2_31_elements():
                    m_scale=shard.m_scale[gs].cpu().numpy(), m_k=shard.m_k[gs].cpu().numpy(),
                    v_codes=shard.v_codes[e].cpu().numpy(), v_scale=shard.v_scale[gs].cpu().numpy(),
                    v_k=shard.v_k[gs].cpu().numpy())
-        compare_step(gpu, ref, G, HP, 3)
+        reps.append(compare_step(gpu, ref, G, HP, 3))
+    print(f"[maxsize] {summary(reps, 'step past 2^31')}", flush=True)
     del shard
 
 
@@ -108,7 +111,9 @@ def test_gemm_output_past_2_31_elements():
     coat.gemm_group_quant(a, b, sa, sb, codes, scales, group_size=G)
     torch.cuda.synchronize()
     sel = np.array([0, 16383, 32768, 65024, M - 1])
-    rc, rs = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(), sa, sb, G)
-    assert np.array_equal(codes[torch.from_numpy(sel).to(DEV)].cpu().numpy(), rc)
+    rc, rs, _, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(), sa, sb, G,
+                                                 want_c=True)
+    assert_codes_near_ties("past 2^31", codes[torch.from_numpy(sel).to(DEV)].cpu().numpy(), rc,
+                           c32.astype(np.float64), G)
     got_s = scales[torch.from_numpy(sel).to(DEV)].cpu().numpy()
     assert np.array_equal(got_s.view(np.uint32), rs.view(np.uint32))

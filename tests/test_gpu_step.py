@@ -10,6 +10,7 @@ import torch
 import oracle
 from adamw_coat_fp8_amd import inputs
 from gpu_util import DEV, bits_np, forced_step_check, lib, require_gpu
+from parity import summary
 
 pytestmark = pytest.mark.gpu
 
@@ -21,13 +22,7 @@ def setup_module():
 
 
 def _log(tag, reps):
-    worst_id = min(min(r["m"]["identical"], r["v"]["identical"]) for r in reps)
-    mism = sum(r["m"]["mismatches"] + r["v"]["mismatches"] for r in reps)
-    print(f"[parity] {tag}: min identical {worst_id:.6f}, mismatched codes {mism}, "
-          f"max rel scale {max(max(r['m']['max_rel_scale'], r['v']['max_rel_scale']) for r in reps):.2e}, "
-          f"max rel k {max(max(r['m']['max_rel_k'], r['v']['max_rel_k']) for r in reps):.2e}, "
-          f"k groups within 1e-5: m {min(r['m']['k_groups_within_1e5'] for r in reps):.5f} "
-          f"v {min(r['v']['k_groups_within_1e5'] for r in reps):.5f}", flush=True)
+    print(f"[parity] {summary(reps, tag)}", flush=True)
 
 
 def test_single_1m_ten_steps():

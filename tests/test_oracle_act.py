@@ -2,19 +2,23 @@
 section 三 "混合粒度激活量化" and eq. FP8量化; transposed FP8 output of the
 non-linear-layer kernels).
 
-Pinned by: torch's FP8 cast on the FP32 products (library), exact power-of-two
-groups (closed form), the format's round-trip error bound, degenerate groups,
-the transpose relation, the memory-overhead row the page prints (golden), and
-the direction of the mixed-granularity claim (per-group error below
-per-tensor error on activations with outliers)."""
+Pinned by: the definition itself in exact rational arithmetic (every code the
+E4M3 value nearest to 448 x / max, ties to even, checked by brute force over
+the format's value set), exact power-of-two groups (closed form), the format's
+round-trip error bound, degenerate groups, the transpose relation, the
+memory-overhead row the page prints (golden), and the direction of the
+mixed-granularity claim (per-group error below per-tensor error on
+activations with outliers)."""
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from e4m3_exact import E4M3_VALUES, group_codes, is_midpoint
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "act_group_overhead.json")
 
@@ -32,18 +36,89 @@ def _act(rows, cols, seed, outliers=True):
     return x.to(torch.bfloat16)
 
 
+def _tie_values(amax, limit=24):
+    """BF16 values x <= amax whose exact quotient 448 x / amax is an E4M3
+    midpoint (exact ties of the rounding), for a group maximum amax."""
+    out = []
+    for lo, hi in zip(E4M3_VALUES, E4M3_VALUES[1:]):
+        x = (lo + hi) / 2 * Fraction(float(amax)) / 448
+        xb = torch.tensor(float(x), dtype=torch.float64).to(torch.bfloat16).double().item()
+        if Fraction(xb) == x:
+            out.append(xb)
+    return out[-limit:]
+
+
+def _check_exact(x, G, codes, scales):
+    rows, cols = x.shape
+    xf = x.float().numpy()
+    for i in range(rows):
+        for j in range(cols // G):
+            grp = xf[i, j * G:(j + 1) * G]
+            amax = np.abs(grp).max()
+            if amax == 0:
+                assert scales[i, j] == 0 and not codes[i, j * G:(j + 1) * G].any()
+                continue
+            assert scales[i, j] == np.float32(amax) / np.float32(448.0)     # S rounded once
+            want = group_codes(grp, amax)
+            got = codes[i, j * G:(j + 1) * G].tolist()
+            assert got == want, (i, j, [(a, b, v) for a, b, v in zip(got, want, grp) if a != b][:4])
+
+
 @pytest.mark.parametrize("G", [16, 32, 64, 128])
-def test_matches_torch_cast_of_fp32_products(G):
-    rows, cols = 37, 4 * G
+def test_matches_exact_definition(G):
+    """Every code equals the E4M3 value nearest to the exact quotient
+    448 x / max (ties to even), computed with fractions; every scale is
+    max / 448 rounded once to FP32."""
+    rows, cols = 12, 4 * G
     x = _act(rows, cols, G)
     codes, scales, codes_t = oracle.quantize_act(_bits(x), rows, cols, G)
+    _check_exact(x, G, codes, scales)
+    assert np.array_equal(codes_t, codes.T)
+
+
+@pytest.mark.parametrize("amax", [3.25, 98.0, 25.5, 12.75, 7.0, 3.0 * 2.0 ** -20, 3.0 * 2.0 ** 99, 5.0 * 2.0 ** -120])
+def test_exact_ties_with_any_group_max(amax):
+    """Groups whose max is not a power of two, filled with values whose exact
+    quotient is an E4M3 midpoint: each goes to the even neighbour, as the
+    definition rounds it."""
+    G = 32
+    ties = _tie_values(amax)
+    assert len(ties) >= 4
+    vals = np.zeros(G, np.float64)
+    vals[0] = amax
+    vals[1:1 + len(ties)] = ties
+    vals[1::3] *= -1
+    x = torch.from_numpy(vals).reshape(1, G).to(torch.bfloat16)
+    assert torch.equal(x.double(), torch.from_numpy(vals).reshape(1, G))    # exact in BF16
+    codes, scales, _ = oracle.quantize_act(_bits(x), 1, G, G)
+    _check_exact(x, G, codes, scales)
+    q = [Fraction(448) * Fraction(v) / Fraction(float(amax)) for v in vals[1:1 + len(ties)]]
+    assert all(is_midpoint(v) for v in q)
+    got = codes[0, 1:1 + len(ties)] & 0x7F
+    assert np.all(got % 2 == 0)                     # the even neighbour
+
+
+def test_fp32_reciprocal_recipe_differs_only_at_exact_ties():
+    """The obvious FP32 recipe, RNE(fl(x * fl(448 / max))), agrees with the
+    definition everywhere except at exact ties whose max is not a power of
+    two (its two roundings push the quotient off the midpoint).  Such ties
+    are common in BF16 activations, well above 1e-4 of the codes here, so a
+    kernel must decide ties exactly to match the definition."""
+    G = 128
+    rows, cols = 37, 4 * G
+    x = _act(rows, cols, G)
+    codes, _, _ = oracle.quantize_act(_bits(x), rows, cols, G, transpose=False)
     xf = x.float().reshape(rows, cols // G, G)
     amax = xf.abs().amax(-1, keepdim=True)
-    r = torch.tensor(448.0, dtype=torch.float32) / amax          # IEEE FP32 division
-    ref = (xf * r).reshape(rows, cols).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    assert np.array_equal(codes, ref)
-    assert np.array_equal(scales, (amax / 448.0).reshape(rows, cols // G).numpy())
-    assert np.array_equal(codes_t, codes.T)
+    r = torch.tensor(448.0, dtype=torch.float32) / amax
+    fp32 = (xf * r).reshape(rows, cols).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    diff = np.argwhere(codes != fp32)
+    assert diff.shape[0] / codes.size > 1e-4
+    am = amax.reshape(rows, cols // G).numpy()
+    for i, j in diff:
+        q = Fraction(448) * Fraction(float(xf.reshape(rows, cols)[i, j])) / Fraction(float(am[i, j // G]))
+        assert is_midpoint(q)
+        assert abs(int(codes[i, j] & 0x7F) - int(fp32[i, j] & 0x7F)) == 1
 
 
 def test_power_of_two_group_closed_form():
@@ -141,9 +216,9 @@ def test_tiny_groups_are_scale_invariant(G):
 
 
 def test_negative_zero_and_signed_underflow():
-    """-0.0 gives code 0x00; a negative value whose scaled magnitude is below
-    half the smallest E4M3 subnormal keeps its sign (0x80); one whose FP32
-    product underflows to -0 gives 0x00."""
+    """-0.0 gives code 0x00; a negative value whose quotient is below half the
+    smallest E4M3 subnormal rounds to zero and keeps its sign (0x80), however
+    small the quotient is."""
     G = 16
     v = np.zeros(G, np.float32)
     v[0] = 1.0
@@ -155,11 +230,12 @@ def test_negative_zero_and_signed_underflow():
     assert c[0, 0] == 0x7E and c[0, 1] == 0x00 and c[0, 2] == 0x80 and c[0, 3] == 0x00
     w = np.zeros(G, np.float32)
     w[0] = 1e30
-    w[1] = -1e-20                 # 448e-50 underflows FP32 to -0 -> 0x00
-    w[2] = -1e-5                  # tiny normal FP32 product -> 0x80
+    w[1] = -1e-20                 # quotient -4.5e-48, below FP32's range -> 0x80
+    w[2] = -1e-5                  # quotient -4.5e-33 -> 0x80
+    w[3] = -0.0
     y = torch.from_numpy(w).reshape(1, G).to(torch.bfloat16)
     c, _, _ = oracle.quantize_act(_bits(y), 1, G, G)
-    assert c[0, 1] == 0x00 and c[0, 2] == 0x80
+    assert c[0, 1] == 0x80 and c[0, 2] == 0x80 and c[0, 3] == 0x00
 
 
 def test_ties_round_to_even():

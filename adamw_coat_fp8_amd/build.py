@@ -1,4 +1,6 @@
-"""Build libcoat_fp8.so (gfx950 HIP kernels + C ABI) in the package folder.
+"""Build libcoat_fp8.so (gfx950 HIP kernels + C ABI) in the package folder,
+and libcoat_bench.so, the benchmark's measurement kernel (the math-free copy
+of the step's traffic; not part of the library's C ABI).
 
 hipcc cross-compiles for gfx950 without a GPU.  Packed FP32 instructions are
 disabled (-packed-fp32-ops): the kernels are written as scalar float code.
@@ -11,6 +13,8 @@ ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("coat_fp8.hip", "coat_act.hip", "coat_gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcoat_fp8.so")
+BENCH_SOURCES = [os.path.join(HERE, "csrc", "coat_mix_ceiling.hip")]
+BENCH_LIB = os.path.join(HERE, "libcoat_bench.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -28,12 +32,17 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", LIB + ".tmp", *SOURCES]
+def _compile(lib, sources, verbose, extra=()):
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", lib + ".tmp", *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    os.replace(lib + ".tmp", lib)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    _compile(LIB, SOURCES, verbose, extra)
+    _compile(BENCH_LIB, BENCH_SOURCES, verbose, extra)
     return LIB
 
 

@@ -43,7 +43,14 @@ def _round_up(x: int, a: int) -> int:
 
 
 class FP8AdamWShard:
-    def __init__(self, numels: Sequence[int], group_size: int = 128, device="cuda"):
+    """`storage`, if given, is another shard of the same tensor list whose
+    flat buffers this one takes as its own (views of their first elements):
+    a shard for another group size over the same memory.  Its per-group
+    arrays must be at least as long (the smallest group size has the
+    longest)."""
+
+    def __init__(self, numels: Sequence[int], group_size: int = 128, device="cuda",
+                 storage: "FP8AdamWShard" = None):
         if group_size not in coat.GROUP_SIZES:
             raise ValueError(f"group_size must be one of {coat.GROUP_SIZES}")
         self.numels = [int(n) for n in numels]
@@ -60,17 +67,36 @@ class FP8AdamWShard:
         self.total_elems = off
         self.total_groups = goff
         dev = self.device
-        self.w = torch.zeros(off, dtype=torch.float32, device=dev)
-        self.grad = torch.zeros(off, dtype=torch.bfloat16, device=dev)
-        self.m_codes = torch.zeros(off, dtype=torch.uint8, device=dev)
-        self.v_codes = torch.zeros(off, dtype=torch.uint8, device=dev)
-        self.m_scale = torch.zeros(goff, dtype=torch.float32, device=dev)
-        self.m_k = torch.zeros(goff, dtype=torch.float32, device=dev)
-        self.v_scale = torch.zeros(goff, dtype=torch.float32, device=dev)
-        self.v_k = torch.zeros(goff, dtype=torch.float32, device=dev)
+        if storage is not None:
+            if storage.total_elems < off or storage.total_groups < goff:
+                raise ValueError("storage shard too small for this tensor list and group size")
+            self.w = storage.w[:off]
+            self.grad = storage.grad[:off]
+            self.m_codes = storage.m_codes[:off]
+            self.v_codes = storage.v_codes[:off]
+            self.m_scale = storage.m_scale[:goff]
+            self.m_k = storage.m_k[:goff]
+            self.v_scale = storage.v_scale[:goff]
+            self.v_k = storage.v_k[:goff]
+            self.reset_state()
+        else:
+            self.w = torch.zeros(off, dtype=torch.float32, device=dev)
+            self.grad = torch.zeros(off, dtype=torch.bfloat16, device=dev)
+            self.m_codes = torch.zeros(off, dtype=torch.uint8, device=dev)
+            self.v_codes = torch.zeros(off, dtype=torch.uint8, device=dev)
+            self.m_scale = torch.zeros(goff, dtype=torch.float32, device=dev)
+            self.m_k = torch.zeros(goff, dtype=torch.float32, device=dev)
+            self.v_scale = torch.zeros(goff, dtype=torch.float32, device=dev)
+            self.v_k = torch.zeros(goff, dtype=torch.float32, device=dev)
         self.slots = [self.slot(i) for i in range(len(self.numels))]
         self.call_indices = balanced_calls(self.numels)
         self.calls = [coat.TensorList([self.slots[i] for i in c]) for c in self.call_indices]
+
+    def reset_state(self):
+        """Fresh optimizer state: every moment code, scale and k zero (an
+        all-zero group), as the library defines a new state."""
+        for t in (self.m_codes, self.v_codes, self.m_scale, self.m_k, self.v_scale, self.v_k):
+            t.zero_()
 
     @property
     def num_params(self) -> int:

@@ -15,8 +15,13 @@ change the work or the traffic).
 
 Prints ONE JSON line: Gparam/s over the timed steps, plus the step kernel's
 roofline position (algorithmic bytes per launch / average launch duration,
-HIP events on the launch stream) and the CPU oracle timed on a bounded sample
-on the host cores.
+HIP events on the launch stream), the rate of a math-free kernel that moves
+exactly the step's traffic with its lane layout (libcoat_bench.so: the
+streaming ceiling of this read/write mix, timed on the same shard), the
+stress recipe at G = 128, 64, 32 and 16 (one shard each, alternating timed
+rounds in this process), and the CPU oracle timed on bounded samples on the
+host cores (all threads, and one thread on the single 1024 x 1024 tensor and
+on 64M-parameter slices of the OLMo-1B and Llama-2-7B shapes).
 
 ``--path act_quant`` measures the per-group activation quantizer instead: one
 step quantizes a (tokens x channels) BF16 matrix (default 8192 x 11008: four
@@ -74,6 +79,15 @@ def parse():
                     help="parameters in the oracle's timing sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of known size (PMC calibration)")
+    ap.add_argument("--no-g-sweep", action="store_true",
+                    help="adamw_step without the stress-recipe group-size sweep")
+    ap.add_argument("--g-sweep-only", action="store_true",
+                    help="adamw_step: only the group-size sweep (for profiling it)")
+    ap.add_argument("--allocations", type=int, default=1,
+                    help="adamw_step: time the step on this many successive allocations of "
+                         "the shard in one process (the shard is freed and allocated again)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="adamw_step: only the math-free copy of the step's traffic")
     args = ap.parse_args()
     act = args.path == "act_quant"
     gemm = args.path == "gemm_group_quant"
@@ -124,65 +138,112 @@ def traffic_from_profile(nbytes_per_launch, path=PMC_SUMMARY, sources=STEP_SOURC
         return None
 
 
-def cpu_baseline(specs, G, hp, sample_params, min_seconds=10.0):
-    """The oracle, as it stands, timed on a bounded sample of the workload:
-    the first elements of each tensor (up to 2M per tensor) until the sample is
-    full; warm state from one untimed oracle step; then whole timed steps
-    (steps 2, 3, ...; the gradient of step 2 is reused, which leaves the work
-    unchanged) until at least `min_seconds` of wall time.  Threads
-    split the sample by whole tensors-slices (the oracle is single-threaded
-    C; ctypes releases the GIL)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_slice(specs, G, stds, budget, seed_steps=(1, 2)):
+    """Host copies of the first elements of each tensor of a workload (up to
+    2M per tensor) until `budget` parameters: w, the gradients of steps 1 and
+    2 and zero states, for the oracle."""
     import numpy as np
     import oracle
     from adamw_coat_fp8_amd import inputs
 
-    stds = inputs.grad_stds(len(specs))
-    pieces, left = [], sample_params
+    work, left = [], budget
     for i, s in enumerate(specs):
         if left <= 0:
             break
         n = min(s.numel, 2 * 1024 * 1024, left)
         n -= n % G if n >= G else 0
-        pieces.append((i, n))
-        left -= n
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    work = []
-    for i, n in pieces:
         w = inputs.weights(n, i, "cpu").numpy().copy()
-        g1 = inputs.bf16_bits(inputs.gradient(n, stds[i], 1, i, "cpu")).numpy().view(np.uint16).copy()
-        g2 = inputs.bf16_bits(inputs.gradient(n, stds[i], 2, i, "cpu")).numpy().view(np.uint16).copy()
-        work.append([w, g1, g2, oracle.QuantizedState.zeros(n, G), oracle.QuantizedState.zeros(n, G)])
+        gs = [inputs.bf16_bits(inputs.gradient(n, stds[i], t, i, "cpu")).numpy().view(np.uint16).copy()
+              for t in seed_steps]
+        work.append([w, gs, oracle.QuantizedState.zeros(n, G), oracle.QuantizedState.zeros(n, G)])
+        left -= n
+    return work
 
-    def run(item, step):
-        w, g1, g2, m, v = item
-        oracle.adamw_fp8_step(w, g1 if step == 1 else g2, m, v, G, **hp, step=step)
 
-    def timed(items, nthreads, seconds):
-        steps = 0
-        with cf.ThreadPoolExecutor(nthreads) as ex:
-            t0 = time.perf_counter()
-            while True:
-                list(ex.map(lambda it: run(it, 2 + steps), items))
-                steps += 1
-                dt = time.perf_counter() - t0
-                if dt >= seconds:
-                    return steps, dt
+def _oracle_step(item, step, G, hp):
+    import oracle
+    w, gs, m, v = item
+    oracle.adamw_fp8_step(w, gs[min(step, len(gs)) - 1], m, v, G, **hp, step=step)
 
+
+def cpu_baseline(specs, G, hp, sample_params, min_seconds=8.0):
+    """The oracle, as it stands, timed on bounded samples on the host cores.
+
+    value: all threads (up to 16) over a `sample_params` sample of the
+    workload -- the first elements of each tensor (up to 2M per tensor),
+    warm state from one untimed oracle step, then whole timed steps (the
+    gradient of step 2 is reused, which leaves the work unchanged) until
+    `min_seconds`; threads split the sample by tensor slices (the oracle is
+    single-threaded C; ctypes releases the GIL).
+
+    single_core: the same oracle on one thread over the single 1024 x 1024
+    tensor, all 10 steps from zero state, and over 64M-parameter slices of the
+    OLMo-1B and Llama-2-7B shapes, one step each from a warm state (made by
+    one untimed step on all threads)."""
+    import numpy as np
+    import oracle
+    from adamw_coat_fp8_amd import inputs
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    stds = inputs.grad_stds(len(specs))
+    work = _oracle_slice(specs, G, stds, sample_params)
     with cf.ThreadPoolExecutor(threads) as ex:
-        list(ex.map(lambda it: run(it, 1), work))
-    steps, dt = timed(work, threads, min_seconds)
-    n_total = sum(n for _, n in pieces)
-    # the same oracle on one host thread, over the first few slices of the sample
-    one = work[:4]
-    n_one = sum(it[0].size for it in one)
-    steps1, dt1 = timed(one, 1, min_seconds / 2)
+        list(ex.map(lambda it: _oracle_step(it, 1, G, hp), work))
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(lambda it: _oracle_step(it, 2 + steps, G, hp), work))
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    n_total = sum(it[0].size for it in work)
+    del work
+
+    single = {}
+    # single 1024 x 1024 tensor, 10 steps from zero state, one thread
+    n1 = 1024 * 1024
+    w = inputs.weights(n1, 0, "cpu").numpy().copy()
+    grads = [inputs.bf16_bits(inputs.gradient(n1, 1e-3, t, 0, "cpu")).numpy().view(np.uint16).copy()
+             for t in range(1, 11)]
+    m, v = oracle.QuantizedState.zeros(n1, G), oracle.QuantizedState.zeros(n1, G)
+    t0 = time.perf_counter()
+    for t in range(1, 11):
+        oracle.adamw_fp8_step(w, grads[t - 1], m, v, G, **hp, step=t)
+    dt1 = time.perf_counter() - t0
+    single["single_1m"] = {"value": round(10 * n1 / dt1 / 1e6, 3), "unit": "Mparam/s",
+                           "sample": f"1024x1024 tensor, steps 1-10 from zero state, "
+                                     f"{dt1:.2f} s wall"}
+    for name in ("olmo_1b", "llama2_7b"):
+        wspecs = inputs.workload_specs(name)
+        wstds = inputs.grad_stds(len(wspecs))
+        sl = _oracle_slice(wspecs, G, wstds, 64 * 1024 * 1024)
+        with cf.ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda it: _oracle_step(it, 1, G, hp), sl))    # warm state
+        ns = sum(it[0].size for it in sl)
+        t0 = time.perf_counter()
+        for it in sl:
+            _oracle_step(it, 2, G, hp)
+        dts = time.perf_counter() - t0
+        single[name] = {"value": round(ns / dts / 1e6, 3), "unit": "Mparam/s",
+                        "sample": f"{ns} params (first <=2M elements of the first {len(sl)} "
+                                  f"tensors), step 2 after an untimed step 1, {dts:.2f} s wall"}
+        del sl
     return {"value": steps * n_total / dt / 1e9, "unit": "Gparam/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n_total} params: first <=2M elements of the first {len(pieces)} "
-                      f"tensors, {steps} whole steps after one untimed step, {dt:.2f} s wall",
-            "single_core": {"value": steps1 * n_one / dt1 / 1e9, "unit": "Gparam/s", "cores": 1,
-                            "sample": f"{n_one} params (the first {len(one)} slices), "
-                                      f"{steps1} whole steps, {dt1:.2f} s wall"}}
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{n_total} params: first <=2M elements of the first tensors, "
+                      f"{steps} whole steps after one untimed step, {dt:.2f} s wall",
+            "single_core": dict(single, cores=1)}
 
 
 def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):
@@ -650,6 +711,105 @@ def bench_codec(args):
     print(json.dumps(rec), flush=True)
 
 
+BENCH_LIB = os.path.join(ROOT, "adamw_coat_fp8_amd", "libcoat_bench.so")
+G_SWEEP = (128, 64, 32, 16)
+
+
+def mix_ceiling(shard, reps: int = 10):
+    """The math-free copy of the step's traffic (libcoat_bench.so) over the
+    whole flat shard, in place and value-preserving: average GB/s of
+    algorithmic bytes per launch over `reps` launches (HIP events on the
+    launch stream), after two untimed launches."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(BENCH_LIB)
+    vp = ctypes.c_void_p
+    lib.coat_bench_mix_ceiling.restype = ctypes.c_int
+    lib.coat_bench_mix_ceiling.argtypes = [vp] * 8 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                                      ctypes.c_uint32, vp]
+    stream = torch.cuda.current_stream()
+    G = shard.group_size
+    n = shard.total_elems // 1024 * 1024
+    args = [shard.w.data_ptr(), shard.grad.data_ptr(), shard.m_codes.data_ptr(),
+            shard.v_codes.data_ptr(), shard.m_scale.data_ptr(), shard.m_k.data_ptr(),
+            shard.v_scale.data_ptr(), shard.v_k.data_ptr(), n, shard.total_groups, G, 0,
+            stream.cuda_stream]
+
+    def launch():
+        rc = lib.coat_bench_mix_ceiling(*args)
+        if rc != 0:
+            raise RuntimeError(f"coat_bench_mix_ceiling returned {rc}")
+
+    launch()
+    launch()
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    nbytes = 14 * n + 32 * (n // G)
+    return nbytes / (ms * 1e-3) / 1e9, ms, nbytes
+
+
+def time_shard_steps(shard, t, hp, stream, steps, per_launch=False):
+    """`steps` timed steps of a warm shard (HIP events around each step, or
+    around each launch): returns (per-step ms list, per-launch ms list)."""
+    import torch
+    n_calls = len(shard.calls)
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+               for _ in range(n_calls)] for _ in range(steps)]
+    for k in range(steps):
+        shard.step(t + 1 + k, **hp, stream=stream, events=events[k])
+    torch.cuda.synchronize()
+    step_ms = [events[k][0][0].elapsed_time(events[k][-1][1]) for k in range(steps)]
+    launch_ms = [events[k][j][0].elapsed_time(events[k][j][1])
+                 for k in range(steps) for j in range(n_calls)]
+    return step_ms, launch_ms
+
+
+def g_sweep(numels, hp, stream, rounds=3, steps=5):
+    """The stress recipe at every group size over the same device buffers
+    (one allocation sized for the smallest G, so that the physical pages
+    behind the shard are the same for every G), in alternating rounds: per
+    round and G, fresh state and weights, 3 untimed steps from zero state,
+    one more untimed step, then `steps` timed steps."""
+    import torch
+    from adamw_coat_fp8_amd import inputs
+    from adamw_coat_fp8_amd.shard import FP8AdamWShard
+
+    stds = inputs.grad_stds(len(numels))
+    base = FP8AdamWShard(numels, group_size=min(G_SWEEP), device="cuda")
+    per = {G: [] for G in G_SWEEP}
+    for r in range(rounds):
+        for G in G_SWEEP:
+            sh = FP8AdamWShard(numels, group_size=G, device="cuda", storage=base)
+            inputs.fill_weights(sh)
+            for t in (1, 2, 3):
+                inputs.fill_gradients(sh, t, stds, "stress")
+                sh.step(t, **hp, stream=stream)
+            sh.step(4, **hp, stream=stream)
+            ms, _ = time_shard_steps(sh, 4, hp, stream, steps)
+            per[G].extend(ms)
+        print(f"[bench] G sweep round {r} done", file=sys.stderr, flush=True)
+    n = sum(numels)
+    out = {}
+    for G in G_SWEEP:
+        med = sorted(per[G])[len(per[G]) // 2]
+        nbytes = sum(algorithmic_bytes(x, G) for x in numels)
+        out[str(G)] = {"Gparam_s": round(n / (med * 1e-3) / 1e9, 1),
+                       "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+                       "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "step_ms_median": round(med, 4), "steps_timed": len(per[G])}
+    del base, sh
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -663,6 +823,10 @@ def main():
         return bench_gemm(args)
     if args.path == "codec":
         return bench_codec(args)
+    return bench_step(args)
+
+
+def bench_step(args):
     import torch
     from adamw_coat_fp8_amd import coat, inputs
     from adamw_coat_fp8_amd.shard import FP8AdamWShard
@@ -675,12 +839,21 @@ def main():
     print(f"[bench] workload {args.workload}: {len(specs)} tensors, {n_params} params, "
           f"G={G}", file=sys.stderr, flush=True)
     torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    if args.g_sweep_only:
+        print(json.dumps({"g_sweep": g_sweep(numels, hp, stream)}), flush=True)
+        return
     shard = FP8AdamWShard(numels, group_size=G, device="cuda")
     stds = inputs.grad_stds(len(specs))
     inputs.fill_weights(shard)
+    if args.ceiling_only:
+        inputs.fill_gradients(shard, 1, stds)
+        gbps, ms, nbytes = mix_ceiling(shard, max(args.steps, 2))
+        print(json.dumps({"mix_ceiling_GBps": round(gbps, 1), "avg_launch_ms": round(ms, 4),
+                          "bytes_per_launch": nbytes}), flush=True)
+        return
     call_lists = shard.calls
     call_bytes = [sum(algorithmic_bytes(numels[i], G) for i in c) for c in shard.call_indices]
-    stream = torch.cuda.current_stream()
 
     def step(t, events=None):
         shard.step(t, **hp, stream=stream, events=events)
@@ -716,13 +889,39 @@ def main():
           f"{len(call_lists)} launches/step, avg launch {avg_launch_ms:.3f} ms",
           file=sys.stderr, flush=True)
 
+    ceiling_gbps, ceiling_ms, _ = mix_ceiling(shard)
+    print(f"[bench] math-free copy of the step's traffic: {ceiling_gbps:.1f} GB/s "
+          f"({ceiling_ms:.3f} ms per launch over the whole shard)", file=sys.stderr, flush=True)
     if args.copy_probe:
         copy_probe()
+
+    per_alloc = []
+    if args.allocations > 1:
+        per_alloc.append(round(n_params / (step_ms[len(step_ms) // 2] * 1e-3) / 1e9, 1))
+        for r in range(1, args.allocations):
+            del shard
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            shard = FP8AdamWShard(numels, group_size=G, device="cuda")
+            inputs.fill_weights(shard)
+            inputs.fill_gradients(shard, 1, stds)
+            for tt in (1, 2, 3):
+                shard.step(tt, **hp, stream=stream)
+            ms, _ = time_shard_steps(shard, 3, hp, stream, args.steps)
+            per_alloc.append(round(n_params / (sorted(ms)[len(ms) // 2] * 1e-3) / 1e9, 1))
+            print(f"[bench] allocation {r}: {per_alloc[-1]} Gparam/s", file=sys.stderr, flush=True)
 
     traffic = traffic_from_profile(bytes_per_launch)
     value = n_params / (ms_per_step * 1e-3) / 1e9
     ceiling = copy_ceiling_gbps()
     total_bytes = sum(call_bytes)
+    sweep = None
+    if not args.no_g_sweep:
+        del shard
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        print("[bench] stress recipe, group-size sweep ...", file=sys.stderr, flush=True)
+        sweep = g_sweep(numels, hp, stream)
     rec = {
         "metric": "Gparam/s per fused FP8-AdamW step + achieved HBM GB/s (% of peak), 1 GPU",
         "value": round(value, 3),
@@ -747,6 +946,8 @@ def main():
             "launches_per_step": len(call_lists),
             "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
             "step_ms_min": round(step_ms[0], 4),
+            "mix_ceiling_GBps": round(ceiling_gbps, 1),
+            "frac_of_mix_ceiling": round(achieved / ceiling_gbps, 4),
             "copy_ceiling_GBps": round(ceiling, 1),
             "kernel_frac_of_copy_ceiling": round(achieved / ceiling, 4),
         },
@@ -762,8 +963,12 @@ def main():
             "avg_launch_ms": round(avg_launch_ms, 4),
         },
     }
+    if per_alloc:
+        rec["config"]["per_allocation_Gparam_s"] = per_alloc
+    if sweep is not None:
+        rec["config"]["stress_g_sweep"] = sweep
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample ...", file=sys.stderr, flush=True)
+        print("[bench] timing the CPU oracle on samples ...", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(specs, G, hp, args.cpu_sample)
     print(json.dumps(rec), flush=True)
 

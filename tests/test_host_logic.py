@@ -135,3 +135,22 @@ def test_bench_codec_byte_accounting():
     import bench
     assert bench.codec_bytes(128 * 1024, 128) == 5 * 128 * 1024 + 8 * 1024
     assert bench.codec_bytes(1000, 16) == 5 * 1000 + 8 * 63
+
+
+def test_shard_over_another_shards_storage():
+    """A shard for another group size built over an existing shard's buffers
+    shares its memory, starts from fresh (zero) state, and rejects storage
+    whose per-group arrays are too short."""
+    from adamw_coat_fp8_amd.shard import FP8AdamWShard
+    numels = [1000, 4096 + 5, 3 * 128, 17]
+    base = FP8AdamWShard(numels, group_size=16, device="cpu")
+    base.m_codes.fill_(7)
+    base.v_scale.fill_(1.5)
+    sh = FP8AdamWShard(numels, group_size=128, device="cpu", storage=base)
+    assert sh.w.data_ptr() == base.w.data_ptr() and sh.m_k.data_ptr() == base.m_k.data_ptr()
+    assert not sh.m_codes.any() and not sh.v_scale.any()
+    assert sh.total_groups == sum(-(-n // 128) for n in numels)
+    for i, n in enumerate(numels):
+        assert sh.slot(i).w.numel() == n
+    with pytest.raises(ValueError):
+        FP8AdamWShard(numels, group_size=16, device="cpu", storage=sh)

@@ -167,7 +167,7 @@ def num_groups(n: int, group_size: int) -> int:
     return (n + group_size - 1) // group_size
 
 
-@dataclass
+@dataclass(frozen=True)
 class QuantState:
     """One FP8 moment on the device: codes uint8[n], scale/k float32[ng]."""
     codes: torch.Tensor
@@ -194,9 +194,12 @@ class QuantState:
                       f"{name}.k": self.k})
 
 
-@dataclass
+@dataclass(frozen=True)
 class ParamSlot:
-    """One tensor of an optimizer shard: FP32 weights, BF16 gradient, m, v."""
+    """One tensor of an optimizer shard: FP32 weights, BF16 gradient, m, v.
+    Frozen, like QuantState: a TensorList copies the tensors' device pointers
+    once, so a slot's tensors cannot be swapped after it is built (build a new
+    slot, e.g. with dataclasses.replace, and a new TensorList instead)."""
     w: torch.Tensor
     grad: torch.Tensor
     m: QuantState
@@ -219,19 +222,23 @@ class ParamSlot:
 
 class TensorList:
     """Marshalled descriptor array for coat_adamw_fp8_step, built once and
-    reused across steps (the pointers stay valid while the tensors live)."""
+    reused across steps (the pointers stay valid while the tensors live: the
+    list holds the slots, and slots are frozen).  The buffer checks run once
+    per group size and again whenever the current device differs from the
+    one they ran on (the library launches on the current device)."""
 
     def __init__(self, slots: Sequence[ParamSlot]):
         self.slots = list(slots)
         self.array = (AdamWTensor * max(1, len(self.slots)))(
             *[s.as_c() for s in self.slots])
-        self._checked = set()   # group sizes the slots have been checked for
+        self._checked = set()   # (group size, device index) the slots have been checked for
 
     def check(self, group_size: int):
-        if group_size not in self._checked:
+        key = (group_size, torch.cuda.current_device() if torch.cuda.is_initialized() else -1)
+        if key not in self._checked:
             for i, slot in enumerate(self.slots):
                 slot.check(group_size, f"tensors[{i}]")
-            self._checked.add(group_size)
+            self._checked.add(key)
 
     def __len__(self):
         return len(self.slots)

@@ -849,6 +849,9 @@ def bench_step(args):
     if args.ceiling_only:
         inputs.fill_gradients(shard, 1, stds)
         gbps, ms, nbytes = mix_ceiling(shard, max(args.steps, 2))
+        print(f"[bench] math-free copy: avg launch {ms:.4f} ms", file=sys.stderr, flush=True)
+        if args.copy_probe:
+            copy_probe()
         print(json.dumps({"mix_ceiling_GBps": round(gbps, 1), "avg_launch_ms": round(ms, 4),
                           "bytes_per_launch": nbytes}), flush=True)
         return

@@ -1,6 +1,8 @@
 """The Python binding's buffer checks, on the CPU: wrong dtype, layout, size
 or device raises ValueError before the library is called (the C ABI sees only
 raw pointers and cannot check buffer sizes)."""
+import dataclasses
+
 import pytest
 import torch
 
@@ -55,9 +57,12 @@ def test_step_and_codec_checks(coat):
     with pytest.raises(ValueError, match="device"):
         coat.adamw_fp8_step([slot], lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,
                             weight_decay=0.1, step=1, group_size=G)
+    m64 = coat.QuantState.zeros(n, 64, "cpu")
     short = coat.ParamSlot(torch.zeros(n), torch.zeros(n, dtype=torch.bfloat16),
-                           coat.QuantState.zeros(n, 64, "cpu"), coat.QuantState.zeros(n, G, "cpu"))
-    short.m.scale = short.m.scale[:5]
+                           dataclasses.replace(m64, scale=m64.scale[:5]),
+                           coat.QuantState.zeros(n, G, "cpu"))
+    with pytest.raises(dataclasses.FrozenInstanceError):
+        short.m.scale = m64.scale                  # a built slot cannot change its buffers
     with pytest.raises(ValueError, match="tensors\\[0\\].m.scale"):
         coat.adamw_fp8_step([short], lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-8,
                             weight_decay=0.1, step=1, group_size=G)

@@ -81,6 +81,8 @@ def parse():
                     help="also run a plain device copy of known size (PMC calibration)")
     ap.add_argument("--no-g-sweep", action="store_true",
                     help="adamw_step without the stress-recipe group-size sweep")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="adamw_step without the OLMo-1B and Llama-2-13B shapes")
     ap.add_argument("--g-sweep-only", action="store_true",
                     help="adamw_step: only the group-size sweep (for profiling it)")
     ap.add_argument("--allocations", type=int, default=1,
@@ -810,6 +812,41 @@ def g_sweep(numels, hp, stream, rounds=3, steps=5):
     return out
 
 
+OTHER_WORKLOADS = (("olmo_1b", 100, 10), ("llama2_13b", 5, 10))   # (shape, warm-up, timed)
+
+
+def time_workload(name, G, hp, stream, warm, steps):
+    """One shape of the default gradient recipe on its own shard: `warm`
+    untimed steps of state history (a fresh gradient each), then `steps`
+    timed steps (HIP events around each step); median step time."""
+    import torch
+    from adamw_coat_fp8_amd import inputs
+    from adamw_coat_fp8_amd.shard import FP8AdamWShard
+
+    specs = inputs.workload_specs(name)
+    numels = [x.numel for x in specs]
+    stds = inputs.grad_stds(len(specs))
+    sh = FP8AdamWShard(numels, group_size=G, device="cuda")
+    inputs.fill_weights(sh)
+    for t in range(1, warm + 1):
+        inputs.fill_gradients(sh, t, stds)
+        sh.step(t, **hp, stream=stream)
+    torch.cuda.synchronize()
+    ms, _ = time_shard_steps(sh, warm, hp, stream, steps)
+    med = sorted(ms)[len(ms) // 2]
+    n = sum(numels)
+    nbytes = sum(algorithmic_bytes(x, G) for x in numels)
+    del sh
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    print(f"[bench] {name}: {n / (med * 1e-3) / 1e9:.1f} Gparam/s", file=sys.stderr, flush=True)
+    return {"params": n, "tensors": len(specs), "warmup": warm, "steps_timed": steps,
+            "Gparam_s": round(n / (med * 1e-3) / 1e9, 1),
+            "GBps": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_ms_median": round(med, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -919,10 +956,15 @@ def bench_step(args):
     ceiling = copy_ceiling_gbps()
     total_bytes = sum(call_bytes)
     sweep = None
-    if not args.no_g_sweep:
+    others = {}
+    if not (args.no_g_sweep and args.no_other_workloads):
         del shard
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+    if not args.no_other_workloads and args.workload == "llama2_7b":
+        for name, warm, steps in OTHER_WORKLOADS:
+            others[name] = time_workload(name, G, hp, stream, warm, steps)
+    if not args.no_g_sweep:
         print("[bench] stress recipe, group-size sweep ...", file=sys.stderr, flush=True)
         sweep = g_sweep(numels, hp, stream)
     rec = {
@@ -968,6 +1010,8 @@ def bench_step(args):
     }
     if per_alloc:
         rec["config"]["per_allocation_Gparam_s"] = per_alloc
+    if others:
+        rec["config"]["other_workloads"] = others
     if sweep is not None:
         rec["config"]["stress_g_sweep"] = sweep
     if not args.no_cpu_baseline:

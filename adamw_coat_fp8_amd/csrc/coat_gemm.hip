@@ -22,14 +22,13 @@
 // panels run.  The epilogue finds each group's maximum and quantizes in
 // registers; only the E4M3 codes go through LDS, for row-contiguous stores.
 //
-// Quantization.  With c the FP32 accumulator, the group
-// maximum of |c s| is fl(max |c| * |s|) exactly (rounding is monotone), the
-// stored scale is that maximum / 448, and each code is RNE(c * m) with the
-// per-group multiplier m = fl(s * fl(448 / max)): one rounding of c per
-// element instead of the two of fl(fl(c s) * 448 / max).  Both agree
-// bit for bit when s is a power of two; otherwise they differ by at most one
-// FP32 rounding of the value rounded to E4M3.  Groups whose maximum lies
-// below 2^-100 or past FP32's range take the two-rounding form.
+// Quantization.  With c the FP32 accumulator and C = fl(c s), the group
+// maximum of |C| is fl(max |c| * |s|) exactly (rounding is monotone) and the
+// stored scale is that maximum / 448.  Each code is the E4M3 rounding of the
+// quotient 448 C / max formed by group_quot (coat_common.h): exact at ties,
+// and for C of at most 21 significant bits exact everywhere.  Groups whose
+// maximum lies below 2^-100 take group_quot's 2^64 pre-scale in a second,
+// rarely taken pass.
 
 #include <hip/hip_runtime.h>
 

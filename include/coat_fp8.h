@@ -157,9 +157,13 @@ coat_status_t coat_e4m3_decode(const uint8_t* codes, int64_t n, float* x,
  *            (IEEE division; 0 for an all-zero group).
  *   codes_t  cols x rows E4M3 codes, the transpose of `codes` (written), or
  *            NULL to skip it.
- * Each code is RNE_E4M3(x * r) with r = 448 / max|x| rounded to FP32 and the
- * product rounded to FP32 (groups with max < 2^-100 compute both as if FP32
- * had an unbounded exponent); -0 gives code 0x00, an all-zero group codes 0.
+ * Each code is the E4M3 rounding (nearest, ties to even) of the exact
+ * quotient 448 x / max|x|: the kernel forms it in FP32 with one residual
+ * correction, which lands on every E4M3 value and midpoint exactly, and for
+ * BF16 x no quotient lies close enough to a midpoint for the remaining error
+ * to change a code.  Groups with max < 2^-100 are pre-scaled by 2^64.
+ * -0 gives code 0x00, a negative x that rounds to zero 0x80, an all-zero
+ * group codes 0.
  * cols must be a multiple of group_size.  x, codes and codes_t 16-byte
  * aligned, scales 4-byte aligned; writes into codes_t are 16, 8 or 4 bytes
  * wide when rows is a multiple of 16, 8 or 4, bytes otherwise.
@@ -179,13 +183,13 @@ coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows,
  * into the producing operation; [P1] 核心公式 FP8量化 with S = max|X| / 448).
  *   C = s * A B^T with s = a_scale * b_scale, accumulated in FP32 on the
  *   matrix cores as c = A B^T, then each 1xG group of a row of C is
- *   quantized: S = max|c s| / 448 with max|c s| = fl(max|c| * |s|), and each
- *   code RNE_E4M3(c * m) with m = fl(s * fl(448 / max)) rounded once to FP32
- *   (-0 -> 0x00, all-zero group -> S = 0 and codes 0).  This equals the
- *   quantizer of coat_fp8_quantize_act applied to fl(c s) bit for bit when s
- *   is a power of two, and otherwise to within one FP32 rounding of the
- *   value rounded to E4M3; groups whose max lies below 2^-100 or beyond FP32
- *   are quantized from fl(c s) exactly as coat_fp8_quantize_act does.
+ *   quantized from C = fl(c s): S = max|C| / 448 (max|C| = fl(max|c| * |s|)
+ *   exactly, rounding being monotone) and each code the E4M3 rounding of
+ *   448 C / max|C|, formed as in coat_fp8_quantize_act (exact at every E4M3
+ *   value and midpoint; exact everywhere when C has at most 21 significant
+ *   bits; otherwise a code can differ only for a quotient within about
+ *   2^-21 relative of a midpoint).  -0 -> 0x00, an all-zero group -> S = 0
+ *   and codes 0; groups whose max lies below 2^-100 take the 2^64 pre-scale.
  *   a        M x K E4M3 codes, row-major (read only).
  *   b        N x K E4M3 codes, row-major (read only): the weight of a linear
  *            layer y = x W^T in its usual [out, in] layout.

@@ -63,9 +63,10 @@ __device__ __forceinline__ uint32_t lanes_max_u32(uint32_t v) {
 // ties.  Otherwise q1 is within about half an ulp of a / b: for BF16 x and
 // max, a / b lies at least 2^-13 (relative) from any midpoint (448 x has 11
 // significant bits, midpoint * max 13), so q1 rounds to the same code; for
-// FP32 x the two can differ only within ~2^-23 of a midpoint.  -0.0 is
-// folded to +0 on a (code 0x00); a negative x whose quotient rounds to zero
-// keeps its sign (0x80).
+// FP32 x the two can differ only within ~2^-23 of a midpoint.  Signed
+// zeros need no extra step: for x = -0.0, q0 = -0, the residual is
+// +0 + (-0) = +0 and q1 = +0 + (-0) = +0 (code 0x00), while a negative x
+// whose quotient underflows keeps its sign through both FMAs (0x80).
 struct GroupQuot {
   float c, b, r;
 };
@@ -81,7 +82,7 @@ __device__ __forceinline__ GroupQuot group_quot_setup(float amax) {
 
 __device__ __forceinline__ float group_quot(float x, float c, float b, float r) {
 #pragma clang fp contract(off)
-  const float a = x * c + 0.0f;
+  const float a = x * c;
   const float q0 = a * r;
   return __builtin_fmaf(__builtin_fmaf(-q0, b, a), r, q0);
 }

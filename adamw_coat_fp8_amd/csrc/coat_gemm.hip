@@ -66,7 +66,7 @@ struct GemmParams {
   uint16_t* c_bf16;  // M x N BF16 (plain epilogue)
   int64_t M, N, K;
   int64_t n_tiles;   // tile columns, ceil(N / 256)
-  int64_t tile_base; // first tile of this launch in the tile order
+  int64_t whole;     // tiles of the order computed whole; each later tile runs as two halves
   float scale;       // a_scale * b_scale, rounded to FP32
 };
 
@@ -92,9 +92,10 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 // ------------------------------------------------------ the kernel
 //
-// With kI = 1 a block computes half a tile, 128 x 256 (waves of 32 x 128):
-// when the tiles do not fill the last round of CUs, the last tiles of the
-// order run as two halves each in a second launch.
+// One block computes one tile (kI = 2) or, with kI = 1, half a tile,
+// 128 x 256 (waves of 32 x 128): when the tiles do not fill the last round
+// of CUs, the last tiles of the order run as two halves each, as the last
+// blocks of the same launch.
 //
 // The MFMA takes the B panel rows as its first operand, so each 32 x 32
 // result is a tile of C^T: register r of lane l holds C[row][col] with
@@ -147,7 +148,7 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 
 template <int G, int kEpi, int kI>
-__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) {
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bidx) {
   static_assert(kI == 1 || kI == 2, "row tiles per wave");
   constexpr int kWaveRows = 32 * kI;         // rows of C per wave (128 kI per block)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -156,9 +157,9 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
   // groups of kGroupM tile rows, column by column inside a group, so the A
   // panels of the group stay in the XCD's L2 and each B panel serves kGroupM
   // tiles in a row.
-  // (half tiles: the two halves of a tile are neighbours in the order)
-  const int64_t bidx = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int64_t bid = p.tile_base + (kI == 2 ? bidx : bidx >> 1);
+  // (bidx is the block's place in the order of its part, whole or half
+  // tiles; the two halves of a tile are neighbours)
+  const int64_t bid = kI == 2 ? bidx : p.whole + (bidx >> 1);
   const int64_t m_tiles = (p.M + kBM - 1) / kBM;
   const int64_t group = bid / (kGroupM * p.n_tiles), first_m = group * kGroupM;
   const int64_t gm = m_tiles - first_m < kGroupM ? m_tiles - first_m : kGroupM;
@@ -483,20 +484,28 @@ __global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) 
   }
 }
 
-// The kernel for whole tiles or half tiles.
+// One launch: blocks 0 .. whole - 1 compute whole tiles, the blocks after
+// them half tiles.  Blocks are dispatched in index order, so the half tiles
+// go to the CUs that finish their whole tiles first, with no launch boundary
+// in between.  Workgroups are dealt to the XCDs round-robin; whole is a
+// multiple of the CU count (so of 8), and each part is mapped XCD-contiguous
+// on its own.
 template <int G, int kEpi>
-const void* kernel_fn(bool half) {
-  return half ? reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kEpi, 1>)
-              : reinterpret_cast<const void*>(&gemm_fp8_kernel<G, kEpi, 2>);
+__global__ __launch_bounds__(kThreads) void gemm_fp8_kernel(const GemmParams p) {
+  const int64_t b = blockIdx.x;
+  if (b < p.whole)
+    gemm_tile<G, kEpi, 2>(p, xcd_contiguous(b, p.whole));
+  else
+    gemm_tile<G, kEpi, 1>(p, xcd_contiguous(b - p.whole, (int64_t)gridDim.x - p.whole));
 }
 
-const void* gemm_kernel_for(int32_t g, int epi, bool half) {
-  if (epi == kBF16) return kernel_fn<128, kBF16>(half);
+const void* gemm_kernel_for(int32_t g, int epi) {
+  if (epi == kBF16) return reinterpret_cast<const void*>(&gemm_fp8_kernel<128, kBF16>);
   switch (g) {
-    case 16: return kernel_fn<16, kGroupQuant>(half);
-    case 32: return kernel_fn<32, kGroupQuant>(half);
-    case 64: return kernel_fn<64, kGroupQuant>(half);
-    default: return kernel_fn<128, kGroupQuant>(half);
+    case 16: return reinterpret_cast<const void*>(&gemm_fp8_kernel<16, kGroupQuant>);
+    case 32: return reinterpret_cast<const void*>(&gemm_fp8_kernel<32, kGroupQuant>);
+    case 64: return reinterpret_cast<const void*>(&gemm_fp8_kernel<64, kGroupQuant>);
+    default: return reinterpret_cast<const void*>(&gemm_fp8_kernel<128, kGroupQuant>);
   }
 }
 
@@ -515,8 +524,8 @@ coat_status_t check_gemm_shape(const uint8_t* a, const uint8_t* b, float a_scale
 
 // One block runs per CU.  When the tiles leave the last round of CUs at most
 // half full, the whole rounds run as 256 x 256 tiles and the remaining tiles
-// of the order as two 128 x 256 halves each, in a second launch on the same
-// stream: half a round instead of a full one.
+// of the order as two 128 x 256 halves each: half a round instead of a full
+// one.
 hipError_t launch_gemm(GemmParams& p, int32_t group_size, int epi, hipStream_t stream) {
   void* args[] = {&p};
   p.n_tiles = (p.N + kBN - 1) / kBN;
@@ -525,16 +534,10 @@ hipError_t launch_gemm(GemmParams& p, int32_t group_size, int epi, hipStream_t s
   hipError_t e = current_cu_count(&cus);
   if (e != hipSuccess) return e;
   const int64_t rem = cus > 0 ? tiles % cus : 0;
-  const int64_t whole = rem > 0 && 2 * rem <= cus ? tiles - rem : tiles;
-  p.tile_base = 0;
-  if (whole > 0) {
-    e = hipLaunchKernel(gemm_kernel_for(group_size, epi, false), dim3((unsigned)whole), dim3(kThreads),
-                        args, 0, stream);
-    if (e != hipSuccess || whole == tiles) return e;
-  }
-  p.tile_base = whole;
-  return hipLaunchKernel(gemm_kernel_for(group_size, epi, true), dim3((unsigned)(2 * (tiles - whole))),
-                         dim3(kThreads), args, 0, stream);
+  p.whole = rem > 0 && 2 * rem <= cus ? tiles - rem : tiles;
+  const int64_t blocks = p.whole + 2 * (tiles - p.whole);
+  return hipLaunchKernel(gemm_kernel_for(group_size, epi), dim3((unsigned)blocks), dim3(kThreads), args,
+                         0, stream);
 }
 
 }  // namespace

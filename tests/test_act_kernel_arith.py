@@ -1,11 +1,14 @@
 """CPU check of the activation quantizer kernel's division recipe (host
-logic; no GPU).  The kernel decides each code on q1 = q0 + fma(-q0, b, a) * r
+logic; no GPU).  The kernel decides each code on q1 = fma(fma(-q0, b, a), r, q0)
 with a = x * (7/8) * pre, b = max * pre / 512, r = fl(1/b), q0 = fl(a * r)
-(csrc/coat_act.hip, act_quot).  Here every FP32 step is emulated exactly
-(fractions, rounded once to FP32, ties to even), and the E4M3 rounding of q1
-must equal the definition's rounding of the exact quotient 448 x / max
-(e4m3_exact) on random BF16 groups, on groups built from exact ties with
-maxima that are not powers of two, and on tiny and huge groups."""
+(csrc/coat_common.h, group_quot).  Here every FP32 step is emulated exactly
+(fractions, rounded once to FP32, ties to even, with IEEE signed zeros), and
+the E4M3 rounding of q1 must equal the definition's rounding of the exact
+quotient 448 x / max (e4m3_exact) on random BF16 groups, on groups built from
+exact ties with maxima that are not powers of two, and on tiny and huge
+groups; -0.0 must come out as +0 (code 0x00) and a negative quotient that
+underflows as -0 (0x80)."""
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -33,20 +36,47 @@ def f32(fr: Fraction) -> Fraction:
     return sign * lo * quantum
 
 
+# An FP32 value as (magnitude-carrying Fraction, sign bit); the sign bit
+# matters only for zeros, which IEEE arithmetic keeps signed.
+def _val(x: float):
+    return (Fraction(x), math.copysign(1.0, x) < 0)
+
+
+def _round(exact: Fraction, zero_neg: bool):
+    """One IEEE rounding to FP32 of an exact result; zero_neg is the sign an
+    exact zero takes.  A nonzero result that rounds to zero keeps its sign."""
+    if exact == 0:
+        return (Fraction(0), zero_neg)
+    return (f32(exact), exact < 0)
+
+
+def _mul(x, y):
+    return _round(x[0] * y[0], x[1] != y[1])
+
+
+def _fma(x, y, z):
+    """x * y + z, one rounding.  An exact zero sum is -0 only when both the
+    product and the addend are negative zeros (round to nearest)."""
+    p = x[0] * y[0]
+    p_neg = x[1] != y[1]
+    both_neg_zero = p == 0 and z[0] == 0 and p_neg and z[1]
+    return _round(p + z[0], both_neg_zero)
+
+
 def kernel_code(x: float, amax: float) -> int:
     """E4M3 code of x as the kernel computes it, every FP32 step exact."""
     pre = Fraction(2) ** 64 if amax < 2.0 ** -100 else Fraction(1)
-    c = Fraction(7, 8) * pre
-    b = f32(Fraction(amax) * pre / 512)
-    r = f32(1 / b)
-    a = f32(Fraction(x) * c)              # exact for BF16 x (asserted below)
-    assert a == Fraction(x) * c
-    q0 = f32(a * r)
-    e = f32(a - q0 * b)                   # FMA: one rounding
-    q1 = f32(e * r + q0)                  # FMA: one rounding
-    if q1 == 0:                           # an underflow keeps the sign of a nonzero x
-        return 0x80 if x < 0 else 0x00
-    return nearest_code(q1)
+    c = (Fraction(7, 8) * pre, False)
+    b = (f32(Fraction(amax) * pre / 512), False)
+    r = (f32(1 / b[0]), False)
+    a = _mul(_val(x), c)                  # exact for BF16 x (asserted below)
+    assert a[0] == Fraction(x) * c[0]
+    q0 = _mul(a, r)
+    e = _fma((-q0[0], not q0[1]), b, a)
+    q1 = _fma(e, r, q0)
+    if q1[0] == 0:                        # the cvt keeps the sign of a zero
+        return 0x80 if q1[1] else 0x00
+    return nearest_code(q1[0])
 
 
 def exact_code(x: float, amax: float) -> int:
@@ -92,3 +122,18 @@ def test_group_max_and_signed_zero():
         assert kernel_code(-0.0, amax) == 0x00
     # a quotient far below FP32's range still rounds to a signed zero
     assert kernel_code(-float(_bf16(1e-20)), float(_bf16(1e30))) == 0x80
+
+
+def test_signed_zero_helpers_follow_ieee():
+    """The emulation's zero signs against the host's IEEE doubles, on operands
+    (signed zeros and ones) where every product and sum is exact."""
+    vals = (0.0, -0.0, 1.0, -1.0)
+    for x in vals:
+        for y in vals:
+            want = x * y
+            got = _mul(_val(x), _val(y))
+            assert got[0] == Fraction(want) and got[1] == (math.copysign(1.0, want) < 0)
+            for z in vals:
+                want = x * y + z
+                got = _fma(_val(x), _val(y), _val(z))
+                assert got[0] == Fraction(want) and got[1] == (math.copysign(1.0, want) < 0), (x, y, z)

@@ -148,7 +148,7 @@ def test_folded_multiplier_exact_inputs(G, shape):
     with np.errstate(divide="ignore", invalid="ignore"):
         bq = (amax * np.float32(2.0 ** -9)).astype(np.float32)[..., None]
         rq = np.where(bq > 0, np.float32(1.0) / bq, np.float32(0.0)).astype(np.float32)
-    aq = (cs.reshape(M, N // G, G) * np.float32(0.875) + np.float32(0.0)).astype(np.float32)
+    aq = (cs.reshape(M, N // G, G) * np.float32(0.875)).astype(np.float32)
     q0 = (aq * rq).astype(np.float32)
     # the exact residual and the correction fit in a double (one rounding each)
     e = (f64(aq) - f64(q0) * f64(bq)).astype(np.float32)
@@ -163,6 +163,31 @@ def test_folded_multiplier_exact_inputs(G, shape):
     step = np.abs(signed_ordinal(gc).astype(np.int64) - signed_ordinal(rc).astype(np.int64))
     print(f"[gemm] folded multiplier: {np.mean(step == 0):.6f} of codes as the definition's", flush=True)
     assert step.max() <= 1
+
+
+@pytest.mark.parametrize("G", [16, 128])
+def test_negative_scale_signed_zeros(G):
+    """s = -0.5 * 2 = -1: every zero accumulator becomes C = -0, which the
+    contract codes as 0x00, beside negative nonzero values in the same group.
+    Rows 0-7 of A keep only their first k, and every other row of B has a
+    zero there, so those rows of C alternate exact zeros and nonzeros.  C,
+    scales and codes against the oracle (codes by the near-tie rule), and
+    every -0 of C coded 0x00."""
+    M, N, K = 64, 256, 128
+    a, b, _, _ = inputs.fp8_operands(M, N, K, 11, DEV, "exact")
+    a[:8, 1:] = 0
+    b[::2, 0] = 0
+    sa, sb = -0.5, 2.0
+    print(f"[gemm] negative scale, signed zeros G={G}", flush=True)
+    codes, scales, c64, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(),
+                                                          sa, sb, G, want_c=True)
+    assert np.all(c64 == c32)
+    gpu = _run(a, b, sa, sb, G)
+    _assert_bit_exact(f"negative scale G={G}", gpu, (codes, scales, c32), G)
+    gc, _, g32 = gpu
+    neg_zero = (g32 == 0) & np.signbit(g32)
+    assert neg_zero[:8].sum() >= 8 * N // 2 - 8 and np.any(g32[:8] < 0)
+    assert np.all(gc[neg_zero] == 0x00)
 
 
 @pytest.mark.parametrize("G", [16, 128])
@@ -353,8 +378,8 @@ def test_bf16_epilogue(shape):
 @pytest.mark.parametrize("G", [16, 128])
 def test_whole_rounds_and_half_tiles(G):
     """4000 x 4352: 272 tiles of 256 x 256 on 256 CUs.  The first 256 run as
-    whole tiles, the last 16 of the tile order as 128 x 256 halves in a second
-    launch, among them the last, 160-row tile row.  Exact inputs: scales, C
+    whole tiles, the last 16 of the tile order as 128 x 256 halves (the last
+    blocks of the same launch), among them the last, 160-row tile row.  Exact inputs: scales, C
     and the BF16 output bit for bit against the oracle, codes by the
     near-tie rule."""
     coat = lib()
@@ -374,7 +399,7 @@ def test_whole_rounds_and_half_tiles(G):
 
 
 def test_graph_capture_replays_match_eager():
-    """The layer captured in a HIP graph at a shape that takes both launches
+    """The layer captured in a HIP graph at a shape that takes both tile kinds
     (4000 x 4352: 256 whole tiles, then 32 half tiles) and replayed three
     times, with the outputs reset and eager work between replays: every
     replay's codes, scales and BF16 output equal an eager call's bit for bit."""

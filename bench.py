@@ -303,6 +303,32 @@ def copy_ceiling_gbps(reps: int = 5) -> float:
     return sorted(rates)[len(rates) // 2]
 
 
+def same_shape_copy_gbps(sets, calls: int) -> float:
+    """Rate of torch's copy of each buffer set's BF16 input into a BF16
+    matrix of the same shape (read + write bytes per launch over the mean
+    HIP-event time of a launch), timed exactly as the quantizer is: buffer
+    sets in turn, one event pair per call.  It moves the quantizer's bytes
+    at its shape with no arithmetic, so it is the streaming ceiling of that
+    shape, launch and ramp included."""
+    import torch
+    dsts = [torch.empty_like(s[0]) for s in sets]
+    for k in range(2 * len(sets)):
+        dsts[k % len(sets)].copy_(sets[k % len(sets)][0])
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(calls)]
+    for k in range(calls):
+        events[k][0].record()
+        dsts[k % len(sets)].copy_(sets[k % len(sets)][0])
+        events[k][1].record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in events) / calls
+    nbytes = 2 * sets[0][0].numel() * sets[0][0].element_size()
+    del dsts
+    torch.cuda.synchronize()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def copy_probe():
     """Three 4 GiB device-to-device copies: a kernel of known traffic against
     which the profiler's FETCH_SIZE / WRITE_SIZE counters are scaled."""
@@ -362,6 +388,7 @@ def bench_act(args):
     launch_sorted = sorted(a.elapsed_time(b) for a, b in events)
     nbytes = act_bytes(rows, cols, G, transpose)
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    same_copy = same_shape_copy_gbps(sets, args.steps)
     ceiling = copy_ceiling_gbps()
     if args.copy_probe:
         copy_probe()
@@ -392,6 +419,8 @@ def bench_act(args):
             "launch_ms_min": round(launch_sorted[0], 5),
             "copy_ceiling_GBps": round(ceiling, 1),
             "kernel_frac_of_copy_ceiling": round(achieved / ceiling, 4),
+            "same_shape_copy_GBps": round(same_copy, 1),
+            "kernel_frac_of_same_shape_copy": round(achieved / same_copy, 4),
         },
         "roofline": {
             "bound": "hbm",
@@ -451,14 +480,14 @@ def gemm_tiling(M, N):
     """The library's tile plan for an M x N output: 256 x 256 tiles (the last
     tile column 128 wide when N is an odd multiple of 128), with the tiles of
     a last round that would leave over half the CUs idle run as 128 x 256
-    halves in a second launch."""
+    halves, the last blocks of the same launch."""
     import torch
     tiles = -(-M // 256) * -(-N // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rem = tiles % cus
     if rem == 0 or 2 * rem > cus:
         return f"256x256 ({tiles} tiles)"
-    return f"256x256 ({tiles - rem} tiles) + 128x256 halves of the last {rem} tiles (second launch)"
+    return f"256x256 ({tiles - rem} tiles) + 128x256 halves of the last {rem} tiles (same launch)"
 
 
 def bench_gemm(args):
@@ -519,7 +548,7 @@ def bench_gemm(args):
         lib_mm = lambda: torch._scaled_mm(af, bf.t(), scale_a=one, scale_b=one,
                                           out_dtype=torch.bfloat16)
         lib_mm()
-        _, ms_lib, _ = timed(lib_mm, max(10, args.steps // 4), 3)
+        _, ms_lib, _ = timed(lib_mm, args.steps, args.warmup)
         context["library_fp8_gemm_bf16_ms"] = round(ms_lib, 5)
         context["library_fp8_gemm_bf16_TFLOPs"] = round(flops / (ms_lib * 1e-3) / 1e12, 1)
     except Exception as e:                      # noqa: BLE001 - context only
@@ -560,8 +589,7 @@ def bench_gemm(args):
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"gemm_fp8_kernel<{G}, group quant> (with its half-tile launch, if any: "
-                      f"times are per library call)",
+            "kernel": f"gemm_fp8_kernel<{G}, group quant> (one launch per call)",
             "flops_per_launch": flops,
             "avg_launch_ms": round(ms_launch, 5),
         },

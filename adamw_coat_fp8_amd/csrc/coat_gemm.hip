@@ -177,40 +177,50 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
   // 16-byte-per-lane buffer load fills 1 KB, 8 rows of a panel, lane L
   // landing at byte 16 L.  So lane L carries row R0 + L/8 and the physical
   // chunk L%8, which under the row swizzle holds logical chunk
-  // (L%8) ^ chunk_swz(row); the swizzle is applied on the global side.  Wave
-  // w fills rows 32 w .. 32 w + 31 of each panel with 4 loads.  The buffer
-  // resource holds the panel base, the scalar offset the K position.  A rows
-  // past M re-load row M - 1 and B rows past N row N - 1: their products only
-  // reach output rows and columns that are never stored.  (Buffer loads count
-  // only against vmcnt, so the waits for LDS reads below stay partial while
-  // panel loads are in flight.)
+  // (L%8) ^ chunk_swz(row); the swizzle is applied on the global side.  The
+  // buffer resource holds the panel base, the scalar offset the K position.
+  // A rows past M re-load row M - 1 and B rows past N row N - 1: their
+  // products only reach output rows and columns that are never stored.
+  // (Buffer loads count only against vmcnt, so the waits for LDS reads below
+  // stay partial while panel loads are in flight.)
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.a + m0 * K), (short)0, (int)0xFFFFFFFF, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.b + n0 * K), (short)0, (int)0xFFFFFFFF, 0x00020000);
   const int64_t a_rows = p.M - m0, b_rows = n_valid;
-  uint32_t aoff[4], boff[4];
+  // Wave w fills rows 8 kLA w .. 8 kLA (w + 1) - 1 of the A panel with kLA
+  // loads (kBlockRows / 64: 4 for a whole tile, 2 for a half) and rows
+  // 32 w .. 32 w + 31 of the B panel with kLB = 4.
+  constexpr int kBlockRows = 4 * kWaveRows;   // 256 (whole tile) or 128 (half)
+  constexpr int kLA = kBlockRows / 64, kLB = 4, kL = kLA + kLB;
+  // s_waitcnt immediate for vmcnt(kL), not waiting on expcnt or lgkmcnt
+  // (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8)
+  constexpr int kVmcntStage1 = (kL & 15) | ((kL >> 4) << 14) | (7 << 4) | (15 << 8);
+  uint32_t aoff[kLA], boff[kLB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 32 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < kLA; ++i) {
+    const int row = 8 * (kLA * wave + i) + (lane >> 3);
     const int c = (lane & 7) ^ chunk_swz(row);
     const int arow = row < a_rows ? row : (int)(a_rows - 1);
     aoff[i] = (uint32_t)arow * (uint32_t)K + 16u * (uint32_t)c;
+  }
+#pragma unroll
+  for (int i = 0; i < kLB; ++i) {
+    const int row = 8 * (kLB * wave + i) + (lane >> 3);
+    const int c = (lane & 7) ^ chunk_swz(row);
     const int brow = row < b_rows ? row : (int)(b_rows - 1);
     boff[i] = (uint32_t)brow * (uint32_t)K + 16u * (uint32_t)c;
   }
-  // Load q = 0..7 of a K step: A (even q) or B (odd q), rows 32 wave + 8 (q / 2) + lane / 8
-  // (a half tile's A panel has 128 rows: waves 0-3 load it).
-  const bool a_loader = kI == 2 || wave < 4;
+  // Load q = 0 .. kL - 1 of a K step into stage S: A loads first, then B.
   auto load1 = [&](int64_t k0, auto S, int q) __attribute__((always_inline)) {
     constexpr int st = decltype(S)::value;
     uint8_t* As = lds_part<2 * st>();
     uint8_t* Bs = lds_part<2 * st + 1>();
-    const int i = q >> 1;
-    if (q & 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, Bs + 1024 * (4 * wave + i), 16, (int)boff[i], (int)k0, 0, 0);
-    else if (a_loader)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, As + 1024 * (4 * wave + i), 16, (int)aoff[i], (int)k0, 0, 0);
+    if (q < kLA)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, As + 1024 * (kLA * wave + q), 16, (int)aoff[q], (int)k0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, Bs + 1024 * (kLB * wave + q - kLA), 16, (int)boff[q - kLA],
+                                               (int)k0, 0, 0);
   };
 
   v16f acc[kI][4];
@@ -225,96 +235,89 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
   const int half = lane >> 5, l32 = lane & 31;
   // Operand fragment: lane supplies row l32 of a 32-row tile and the k bytes
   // 64 kk + 32 half .. +31 (logical chunks c0, c0 + 1 of the panel row).
-  auto frag = [&](const uint8_t* panel, int row, int kk) __attribute__((always_inline)) {
-    const int c0 = 4 * kk + 2 * half;
-    const uint4 lo = *reinterpret_cast<const uint4*>(panel + panel_off(row, c0));
-    const uint4 hi = *reinterpret_cast<const uint4*>(panel + panel_off(row, c0 + 1));
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  auto frag_lo = [&](const uint8_t* panel, int row, int kk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(panel + panel_off(row, 4 * kk + 2 * half));
   };
-  // A K step is four MFMA groups g = (kk, h): the wave's kI row tiles against
-  // column tiles 2h, 2h + 1 at k half kk.  The fragments of group g + 1 are read
-  // while the MFMAs of group g run (two register sets fb0 / fb1 for B, one A
-  // set per kk), so the waits on LDS reads are partial.
-  v8i fa0[kI], fa1[kI], fb0[2], fb1[2];
-  auto read_a = [&](v8i* f, const uint8_t* As, int kk) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kI; ++i) f[i] = frag(As, wm * kWaveRows + 32 * i + l32, kk);
+  auto frag_hi = [&](const uint8_t* panel, int row, int kk) __attribute__((always_inline)) {
+    return *reinterpret_cast<const uint4*>(panel + panel_off(row, 4 * kk + 2 * half + 1));
   };
-  auto read_b = [&](v8i* f, const uint8_t* Bs, int kk, int h) __attribute__((always_inline)) {
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) f[jj] = frag(Bs, wn * 128 + 32 * (2 * h + jj) + l32, kk);
-  };
-  // MFMA q (0 .. 2 kI - 1) of a group: row tile q / 2, column tile 2 h + q % 2
-  auto mma1 = [&](const v8i* fa, const v8i* fb, int h, int q) __attribute__((always_inline)) {
-    if (q < 2 * kI) {
-      const int i = q >> 1, jj = q & 1;
-      acc[i][2 * h + jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[jj], fa[i], acc[i][2 * h + jj],
-                                                                          0, 0, 0, 0, 0, 0);
+  // Fragments of the two k halves of a step: set f = kk.  Read r of a set
+  // (0 .. 2 (4 + kI) - 1): B tiles 0-3 first, then A tiles, low 16 bytes then high.
+  uint4 fa[2][kI][2], fb[2][4][2];
+  auto read1 = [&](int f, const uint8_t* As, const uint8_t* Bs, int kk, int r) __attribute__((always_inline)) {
+    if (r < 8) {
+      const int j = r >> 1, row = wn * 128 + 32 * j + l32;
+      fb[f][j][r & 1] = (r & 1) ? frag_hi(Bs, row, kk) : frag_lo(Bs, row, kk);
+    } else {
+      const int i = (r - 8) >> 1, row = wm * kWaveRows + 32 * i + l32;
+      fa[f][i][r & 1] = (r & 1) ? frag_hi(As, row, kk) : frag_lo(As, row, kk);
     }
   };
-  // The eight panel loads of a K step are spread one per MFMA over three
-  // phases: loads 0-2 of step kt + 2 go out in the last phase of step kt,
-  // right after the barrier that frees stage S; loads 3-7 in the first two
-  // phases of step kt + 1; all are waited for at the barrier of step kt + 1.
-  // Past the last step the loads re-fetch the last K slice into a stage that
-  // is not read again.
+  auto as_v8 = [](const uint4* v) __attribute__((always_inline)) {
+    return v8i{(int)v[0].x, (int)v[0].y, (int)v[0].z, (int)v[0].w,
+               (int)v[1].x, (int)v[1].y, (int)v[1].z, (int)v[1].w};
+  };
+  // MFMA n of set f: row tile n / 4, column tile n % 4
+  auto mma1 = [&](int f, int n) __attribute__((always_inline)) {
+    const int i = n >> 2, j = n & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8(fb[f][j]), as_v8(fa[f][i]), acc[i][j],
+                                                                0, 0, 0, 0, 0, 0);
+  };
+  // A K step is two phases of 4 kI MFMAs, one per k half.  Phase 0 runs on
+  // set 0 while set 1 (k half 1 of the same stage) is read.  Then every wave
+  // waits for its reads and for its loads into the other stage, and the block
+  // meets at the one barrier of the step: the stage being computed on has been
+  // read in full, and the other stage is complete.  Phase 1 runs on set 1
+  // while set 0 of the next step is read from the other stage and the loads of
+  // the step after next go into this one, so each load has a whole phase and
+  // more before the barrier that waits for it.  Past the last step the loads
+  // re-fetch the last K slice into a stage that is not read again.
+  constexpr int kMF = 4 * kI, kR = 2 * (4 + kI);
   const int64_t k_last = K - kBK;
   auto kslice = [&](int k) __attribute__((always_inline)) {
     return k < nk ? (int64_t)k * kBK : k_last;
   };
   auto kstep = [&](int kt, auto S) __attribute__((always_inline)) {
     constexpr int st = decltype(S)::value;
-    using N = std::integral_constant<int, 1 - st>;
     const uint8_t* As = lds_part<2 * st>();
     const uint8_t* Bs = lds_part<2 * st + 1>();
-    const int64_t k1 = kslice(kt + 1), k2 = kslice(kt + 2);
-    // on entry fa0 / fb0 hold group (0, 0) of stage S
-    read_b(fb1, Bs, 0, 1);
-    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* An = lds_part<2 * (1 - st)>();
+    const uint8_t* Bn = lds_part<2 * (1 - st) + 1>();
+    const int64_t k2 = kslice(kt + 2);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      mma1(fa0, fb0, 0, q);
-      if (q < 3) load1(k1, N{}, 3 + q);
+    for (int n = 0; n < kMF; ++n) {
+      mma1(0, n);
+#pragma unroll
+      for (int r = n * kR / kMF; r < (n + 1) * kR / kMF; ++r) read1(1, As, Bs, 1, r);
       __builtin_amdgcn_sched_barrier(0);
     }
-    read_b(fb0, Bs, 1, 0);
-    read_a(fa1, As, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      mma1(fa0, fb1, 1, q);
-      if (q < 2) load1(k1, N{}, 6 + q);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    read_b(fb1, Bs, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mma1(fa1, fb0, 0, q);
-    __builtin_amdgcn_sched_barrier(0);
-    // every wave has read all of stage S and waits for its loads of stage
-    // 1 - S; after the barrier stage 1 - S is complete and stage S is free
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // first fragments of the next step (after the last step: read, unused)
-    read_b(fb0, lds_part<2 * (1 - st) + 1>(), 0, 0);
-    read_a(fa0, lds_part<2 * (1 - st)>(), 0);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      mma1(fa1, fb1, 1, q);
-      if (q < 3) load1(k2, S, q);
+    for (int n = 0; n < kMF; ++n) {
+      mma1(1, n);
+#pragma unroll
+      for (int r = n * kR / kMF; r < (n + 1) * kR / kMF; ++r) read1(0, An, Bn, 0, r);
+#pragma unroll
+      for (int q = n * kL / kMF; q < (n + 1) * kL / kMF; ++q) load1(k2, S, q);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   if (nk > 0) {
+    // both stages' loads go out at once; the first barrier waits only for
+    // stage 0 (loads complete in issue order: vmcnt(kL) leaves the kL loads
+    // of stage 1 in flight)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) load1(0, std::integral_constant<int, 0>{}, q);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    for (int q = 0; q < kL; ++q) load1(0, std::integral_constant<int, 0>{}, q);
 #pragma unroll
-    for (int q = 0; q < 3; ++q) load1(kslice(1), std::integral_constant<int, 1>{}, q);
-    read_b(fb0, lds_part<1>(), 0, 0);
-    read_a(fa0, lds_part<0>(), 0);
+    for (int q = 0; q < kL; ++q) load1(kslice(1), std::integral_constant<int, 1>{}, q);
+    // (no release fence here: it would wait for every load, and each wave
+    // has already waited for its own loads of stage 0)
+    __builtin_amdgcn_s_waitcnt(kVmcntStage1);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+    for (int r = 0; r < kR; ++r) read1(0, lds_part<0>(), lds_part<1>(), 0, r);
   }
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {

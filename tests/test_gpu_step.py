@@ -243,3 +243,60 @@ def test_training_trajectory_tracks_fp32_adamw():
     for s in (10, 50, 100):
         want, got = prob.loss(ref[s - 1]), prob.loss(traj[s - 1])
         assert abs(got - want) <= 0.2 * want, (s, got, want)
+
+
+def test_training_trajectory_many_tensors_tracks_fp32_adamw():
+    """The same bar over 64 tensors in one launch: 64 independent copies of
+    the small least-squares problem (4,096 weights each, seeds 0-63, the same
+    sample count, column-scale spread and target law), 262,144 weights in
+    2,048 groups, 400 steps against torch.optim.AdamW with FP32 moments on the
+    same device.  Each run's gradient comes from its own weights (FP32 on the
+    device, rounded to BF16).  Every tensor's weights must stay within 20% of
+    the FP32 run, relative to the distance that run has moved, and the total
+    loss must follow the FP32 run's."""
+    coat = lib()
+    steps, G, nb, d, samples = 400, 128, 64, 4096, 512
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    x = torch.randn(nb, samples, d, generator=gen, device=DEV) / d ** 0.5
+    x *= torch.exp(torch.empty(nb, 1, d, device=DEV).uniform_(np.log(1e-2), np.log(10.0), generator=gen))
+    y = torch.bmm(x, (torch.randn(nb, d, 1, generator=gen, device=DEV) * 0.02))
+    xt = x.transpose(1, 2).contiguous()
+
+    def grad_bf16(w):
+        r = torch.bmm(x, w.view(nb, d, 1)) - y
+        return (torch.bmm(xt, r) / samples).reshape(-1).to(torch.bfloat16)
+
+    def loss(w):
+        r = torch.bmm(x, w.view(nb, d, 1)) - y
+        return 0.5 * float((r * r).mean())
+
+    p = torch.nn.Parameter(torch.zeros(nb * d, dtype=torch.float32, device=DEV))
+    opt = torch.optim.AdamW([p], lr=HP["lr"], betas=(HP["beta1"], HP["beta2"]), eps=HP["eps"],
+                            weight_decay=HP["weight_decay"], foreach=False, fused=False)
+    ref = []
+    for _ in range(steps):
+        p.grad = grad_bf16(p.detach()).float()
+        opt.step()
+        ref.append(p.detach().clone())
+
+    w = torch.zeros(nb * d, dtype=torch.float32, device=DEV)
+    g = torch.zeros(nb * d, dtype=torch.bfloat16, device=DEV)
+    tl = coat.TensorList([coat.ParamSlot(w[b * d:(b + 1) * d], g[b * d:(b + 1) * d],
+                                         coat.QuantState.zeros(d, G, DEV), coat.QuantState.zeros(d, G, DEV))
+                          for b in range(nb)])
+    dev_max, losses = torch.zeros(nb, device=DEV), {}
+    for t in range(1, steps + 1):
+        g.copy_(grad_bf16(w))
+        coat.adamw_fp8_step(tl, **HP, step=t, group_size=G)
+        r = ref[t - 1].view(nb, d)
+        dev = torch.linalg.norm(w.view(nb, d) - r, dim=1) / torch.linalg.norm(r, dim=1)
+        dev_max = torch.maximum(dev_max, dev)
+        if t in (10, 50, 100):
+            losses[t] = (loss(w), loss(ref[t - 1]))
+    torch.cuda.synchronize()
+    dm = dev_max.cpu().numpy()
+    print(f"[trajectory] 64 tensors: max relative deviation from FP32 AdamW per tensor: median "
+          f"{np.median(dm):.3f}, max {dm.max():.3f}; losses {losses}", flush=True)
+    assert dm.max() < 0.2
+    for t, (got, want) in losses.items():
+        assert abs(got - want) <= 0.2 * want, (t, got, want)

@@ -187,7 +187,12 @@ def test_free_running_drift_report():
     where b1*m and (1-b1)*g cancel, so a 1e-7 difference in one step's state
     moves later k values and shifts whole groups of m codes by one step.  It
     reports the drift and bounds what must stay close: the weights (relative
-    to their total update) and the second moment's codes."""
+    to their total update, median and L2), the second moment's codes, and the
+    first moment's values: even where whole groups of m codes moved to another
+    grid, the dequantized values of the two sides stay within about one
+    quantization step of each other, so their L2 difference is held under
+    2^-3 / sqrt(3) of |m| (the RMS of a difference spread over one step of a
+    3-bit-mantissa grid)."""
     coat = lib()
     n, G = 1024 * 1024, 128
     w0 = inputs.weights(n, 0, DEV)
@@ -207,10 +212,20 @@ def test_free_running_drift_report():
     rel = np.abs(wg - wr) / np.maximum(upd, 1e-12)
     same_m = np.mean(m.codes.cpu().numpy() == mr.codes)
     same_v = np.mean(v.codes.cpu().numpy() == vr.codes)
+    w_l2 = np.linalg.norm(wg - wr) / np.linalg.norm(wr - w0.cpu().numpy())
+    def deq(st):
+        return oracle.dequantize_expand(oracle.QuantizedState(st.codes.cpu().numpy(), st.scale.cpu().numpy(),
+                                                              st.k.cpu().numpy()), G)
+    dm, dmr = deq(m), oracle.dequantize_expand(mr, G)
+    dv, dvr = deq(v), oracle.dequantize_expand(vr, G)
+    m_l2 = np.linalg.norm(dm - dmr) / np.linalg.norm(dmr)
+    v_l2 = np.linalg.norm(dv - dvr) / np.linalg.norm(dvr)
     print(f"[drift] 10 free steps: median |dw|/|update| {np.median(rel):.2e}, "
-          f"p99.9 {np.quantile(rel, 0.999):.2e}; identical codes m {same_m:.5f} v {same_v:.5f}",
+          f"p99.9 {np.quantile(rel, 0.999):.2e}; identical codes m {same_m:.5f} v {same_v:.5f}; "
+          f"L2 relative: w (to the update) {w_l2:.2e}, dequantized m {m_l2:.2e}, v {v_l2:.2e}",
           flush=True)
-    assert np.median(rel) < 2e-2 and same_v > 0.99
+    assert np.median(rel) < 2e-2 and w_l2 < 2e-2 and same_v > 0.99
+    assert m_l2 < 2.0 ** -3 / np.sqrt(3.0)
 
 
 def test_training_trajectory_tracks_fp32_adamw():

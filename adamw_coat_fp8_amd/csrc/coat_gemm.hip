@@ -195,6 +195,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
   constexpr int kLA = kBlockRows / 64, kLB = 4, kL = kLA + kLB;
   // s_waitcnt immediate for vmcnt(kL), not waiting on expcnt or lgkmcnt
   // (vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8)
+  static_assert(kL < 64, "vmcnt holds at most 63");
   constexpr int kVmcntStage1 = (kL & 15) | ((kL >> 4) << 14) | (7 << 4) | (15 << 8);
   uint32_t aoff[kLA], boff[kLB];
 #pragma unroll

@@ -462,3 +462,29 @@ def test_bad_arguments_rejected_nothing_written():
         assert g(*cargs, vp(s)) == want, (args, want)
     torch.cuda.synchronize()
     assert torch.equal(codes, snap[0]) and torch.equal(scales, snap[1])
+
+
+def _random_shapes(count=16, seed=2024):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    for _ in range(count):
+        M = int(rng.integers(1, 700))
+        N = 128 * int(rng.integers(1, 9))          # odd and even multiples of 128
+        K = 128 * int(rng.integers(1, 9))          # 1 to 8 K steps, odd and even
+        G = int(rng.choice([16, 32, 64, 128]))
+        shapes.append((M, N, K, G))
+    return shapes
+
+
+@pytest.mark.parametrize("shape", _random_shapes(), ids=lambda s: "x".join(map(str, s)))
+def test_random_shapes_exact_inputs(shape):
+    """Seeded random M (1-699), N and K (128-1024, odd and even multiples of
+    128) and G on exact inputs: C and scales bit for bit against the oracle,
+    codes by the near-tie rule."""
+    M, N, K, G = shape
+    a, b, sa, sb = inputs.fp8_operands(M, N, K, 13, DEV, "exact")
+    print(f"[gemm] random shape {M}x{N}x{K} G={G}", flush=True)
+    codes, scales, c64, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy(), b.cpu().numpy(),
+                                                          sa, sb, G, want_c=True)
+    assert np.all(c64 == c32)
+    _assert_bit_exact(f"random {shape}", _run(a, b, sa, sb, G), (codes, scales, c32), G)

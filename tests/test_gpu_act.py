@@ -181,3 +181,29 @@ def test_empty_is_noop_and_bad_arguments_rejected():
     assert torch.equal(scales.view(torch.int32), snap[1].view(torch.int32))
     with pytest.raises(coat.CoatError):
         coat.quantize_act(x, codes, scales, codes_t, group_size=24)
+
+
+def _random_shapes(count=12, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        G = int(rng.choice([16, 32, 64, 128]))
+        rows = int(rng.integers(1, 2500))
+        cols = G * int(rng.integers(1, 3072 // G + 1))
+        out.append((rows, cols, G, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_shapes(), ids=lambda c: "x".join(map(str, c)))
+def test_random_shapes_bit_exact(case):
+    """Seeded random rows (1-2499), column counts (any multiple of G up to
+    3072) and G, with and without the transpose: codes, scales and transposed
+    codes bit for bit against the oracle."""
+    rows, cols, G, transpose = case
+    x = inputs.activation(rows, cols, 9, DEV, "llm", G)
+    print(f"[act] random {rows}x{cols} G={G} transpose={transpose}", flush=True)
+    gpu = _gpu(x, G, transpose)
+    ref = _oracle(x, G)
+    if not transpose:
+        ref = (ref[0], ref[1], None)
+    _assert_same(f"random {case}", gpu, ref)

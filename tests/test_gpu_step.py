@@ -79,6 +79,42 @@ def test_many_tensors_multiple_launches():
     _log("97 tensors step 3", reps)
 
 
+# Other hyperparameters: classic Adam betas without decay, no first-moment
+# averaging with a large eps and lr, and the OLMo-1B-style recipe; each from a
+# warm state, at an early step and at a late one where both bias corrections
+# are near 1.
+HP_VARIANTS = [
+    dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0),
+    dict(lr=1e-2, beta1=0.0, beta2=0.99, eps=1e-6, weight_decay=0.01),
+    dict(lr=4e-4, beta1=0.9, beta2=0.95, eps=1e-5, weight_decay=0.1),
+]
+
+
+@pytest.mark.parametrize("late", [False, True], ids=["step3", "step10000"])
+@pytest.mark.parametrize("hp_i", range(len(HP_VARIANTS)), ids=["adam", "b1_zero", "olmo"])
+@pytest.mark.parametrize("G", [32, 128])
+def test_hyperparameter_variants(G, hp_i, late):
+    """Ragged tensors (tails, a single element) from a warm oracle state (two
+    oracle steps), then one forced step at step 3 or step 10000, under each
+    hyperparameter set: the same gates as every other step test."""
+    hp = HP_VARIANTS[hp_i]
+    sizes = [1000, 1, 4096 + 5, 128 * 70 + 77, 16384]
+    tens = []
+    for i, n in enumerate(sizes):
+        w = inputs.weights(n, i, DEV).cpu().numpy()
+        m = oracle.QuantizedState.zeros(n, G)
+        v = oracle.QuantizedState.zeros(n, G)
+        steps = (9998, 9999) if late else (1, 2)
+        for t in steps:
+            g = bits_np(inputs.gradient(n, 1e-3, t % 7 + 1, i, DEV))
+            oracle.adamw_fp8_step(w, g, m, v, G, **hp, step=t)
+        g = bits_np(inputs.gradient(n, 1e-3, 5, i, DEV))
+        tens.append(dict(w=w, m=m, v=v, g=g))
+    step = 10000 if late else 3
+    _, reps = forced_step_check(tens, hp, step, G)
+    _log(f"hparams {hp_i} G={G} step {step}", reps)
+
+
 def test_deterministic_and_stream_ordered():
     coat = lib()
     n, G = 300_000 + 11, 64

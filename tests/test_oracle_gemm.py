@@ -106,3 +106,27 @@ def test_zero_rows_nan_codes_and_ragged_groups():
         oracle.gemm_fp8_group_quant(bad, b, 1.0, 1.0, 16)
     with pytest.raises(oracle.OracleError):
         oracle.gemm_fp8_group_quant(a, b[:24], 1.0, 1.0, 16)     # N = 24 not a multiple of G
+
+
+@pytest.mark.parametrize("G", [16, 128])
+def test_negative_scale_flips_signs_and_codes_zero_as_plus(G):
+    """The quantizer is odd: with the scale product negated, every nonzero
+    output's code is its positive-product code with the sign bit flipped
+    (round to nearest even is symmetric), the scales are unchanged, and an
+    exact zero output, now -0, still codes 0x00."""
+    rng = np.random.default_rng(6)
+    M, N, K = 6, 2 * G, 64
+    a, b = _rand_codes(rng, (M, K)), _rand_codes(rng, (N, K))
+    a[0, 1:] = 0                                   # row 0: a[0, 0] * b[j, 0] only
+    b[::2, 0] = 0                                  # ... which is zero for every other j
+    pc, ps, _, pc32 = oracle.gemm_fp8_group_quant(a, b, 0.5, 2.0, G, want_c=True)
+    nc, ns, _, nc32 = oracle.gemm_fp8_group_quant(a, b, -0.5, 2.0, G, want_c=True)
+    assert np.array_equal(ps.view(np.uint32), ns.view(np.uint32))
+    zero = pc32 == 0
+    assert zero.sum() >= N // 2 and np.all(np.signbit(nc32[zero]))
+    assert np.all(nc[zero] == 0x00) and np.all(pc[zero] == 0x00)
+    nz = ~zero & (pc != 0x00)
+    assert np.array_equal(nc[nz], pc[nz] ^ 0x80)
+    # values that round to zero keep their sign: code 0x80 under the negative product
+    under = ~zero & (pc == 0x00)
+    assert np.all(nc[under] == 0x80)

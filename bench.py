@@ -329,6 +329,35 @@ def same_shape_copy_gbps(sets, calls: int) -> float:
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def cast_ceilings_gbps(x, y, calls: int):
+    """Torch's plain casts with the codec's per-element traffic and no group
+    statistics: FP32 -> E4M3 (read 4 B, write 1 B) over the same FP32 state,
+    and E4M3 -> FP32 back into `y`, each timed with an event pair per call.
+    Returns GB/s of 5 B per element for each direction."""
+    import torch
+    f8 = torch.empty(x.numel(), dtype=torch.float8_e4m3fn, device=x.device)
+    f8.copy_(x)
+    y.copy_(f8)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(calls)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / calls
+
+    nbytes = 5 * x.numel()
+    q = nbytes / (timed(lambda: f8.copy_(x)) * 1e-3) / 1e9
+    d = nbytes / (timed(lambda: y.copy_(f8)) * 1e-3) / 1e9
+    del f8
+    torch.cuda.synchronize()
+    return q, d
+
+
 def copy_probe():
     """Three 4 GiB device-to-device copies: a kernel of known traffic against
     which the profiler's FETCH_SIZE / WRITE_SIZE counters are scaled."""
@@ -693,6 +722,7 @@ def bench_codec(args):
           file=sys.stderr, flush=True)
     if args.copy_probe:
         copy_probe()
+    cast_q, cast_d = cast_ceilings_gbps(x, y, args.steps)
     ceiling = copy_ceiling_gbps()
     rec = {
         "metric": "Gelem/s per expand-quantize + dequantize-expand round trip of an FP32 "
@@ -721,6 +751,10 @@ def bench_codec(args):
                                                 "dequantize_hbm_bytes_per_launch"),
             },
             "copy_ceiling_GBps": round(ceiling, 1),
+            "torch_cast_fp32_to_e4m3_GBps": round(cast_q, 1),
+            "quantize_frac_of_cast": round(q_gbs / cast_q, 4),
+            "torch_cast_e4m3_to_fp32_GBps": round(cast_d, 1),
+            "dequantize_frac_of_cast": round(d_gbs / cast_d, 4),
         },
         "roofline": {
             "bound": "hbm",

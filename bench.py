@@ -46,6 +46,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# The activation quantizer's calls last tens of microseconds, and an event
+# pair around every call adds about 2.5 us to each (the event packets between
+# two launches hold the next one back), so its launches are timed in batches
+# of this many back-to-back calls per event pair.
+ACT_CALLS_PER_EVENT = 10
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_adamw_fp8_step_llama2_7b.txt")
 PMC_SUMMARY_ACT = os.path.join(ROOT, "profiles", "pmc_quantize_act_8192x11008.txt")
 PMC_SUMMARY_GEMM = os.path.join(ROOT, "profiles", "pmc_gemm_group_quant_8192x11008x4096.txt")
@@ -303,26 +308,47 @@ def copy_ceiling_gbps(reps: int = 5) -> float:
     return sorted(rates)[len(rates) // 2]
 
 
+def batched_launch_ms(call, calls: int, stream) -> list:
+    """Enqueues `calls` calls of call(k) on `stream`, ACT_CALLS_PER_EVENT
+    back to back between the two events of a pair, and returns the mean
+    time of one launch in each batch (ms), from the HIP events."""
+    import torch
+    nb = -(-calls // ACT_CALLS_PER_EVENT)
+    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(nb)]
+    sizes = []
+    k = 0
+    for e0, e1 in events:
+        n = min(ACT_CALLS_PER_EVENT, calls - k)
+        e0.record(stream)
+        for _ in range(n):
+            call(k)
+            k += 1
+        e1.record(stream)
+        sizes.append(n)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / n for (a, b), n in zip(events, sizes)]
+
+
 def same_shape_copy_gbps(sets, calls: int) -> float:
     """Rate of torch's copy of each buffer set's BF16 input into a BF16
     matrix of the same shape (read + write bytes per launch over the mean
     HIP-event time of a launch), timed exactly as the quantizer is: buffer
-    sets in turn, one event pair per call.  It moves the quantizer's bytes
-    at its shape with no arithmetic, so it is the streaming ceiling of that
-    shape, launch and ramp included."""
+    sets in turn, batches of back-to-back calls per event pair.  It moves
+    the quantizer's bytes at its shape with no arithmetic, so it is the
+    streaming ceiling of that shape, launch and ramp included."""
     import torch
+    stream = torch.cuda.current_stream()
     dsts = [torch.empty_like(s[0]) for s in sets]
+
+    def call(k):
+        dsts[k % len(sets)].copy_(sets[k % len(sets)][0])
+
     for k in range(2 * len(sets)):
-        dsts[k % len(sets)].copy_(sets[k % len(sets)][0])
+        call(k)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-              for _ in range(calls)]
-    for k in range(calls):
-        events[k][0].record()
-        dsts[k % len(sets)].copy_(sets[k % len(sets)][0])
-        events[k][1].record()
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in events) / calls
+    per = batched_launch_ms(call, calls, stream)
+    ms = sum(per) / len(per)
     nbytes = 2 * sets[0][0].numel() * sets[0][0].element_size()
     del dsts
     torch.cuda.synchronize()
@@ -402,19 +428,13 @@ def bench_act(args):
         call(k)
     torch.cuda.synchronize()
     print(f"[bench] {args.warmup} warm-up calls done", file=sys.stderr, flush=True)
-    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        events[k][0].record(stream)
-        call(k)
-        events[k][1].record(stream)
-    torch.cuda.synchronize()
+    per_batch = batched_launch_ms(call, args.steps, stream)
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    avg_launch_ms = sum(a.elapsed_time(b) for a, b in events) / args.steps
-    launch_sorted = sorted(a.elapsed_time(b) for a, b in events)
+    avg_launch_ms = sum(per_batch) / len(per_batch)
+    launch_sorted = sorted(per_batch)
     nbytes = act_bytes(rows, cols, G, transpose)
     achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
     same_copy = same_shape_copy_gbps(sets, args.steps)
@@ -444,6 +464,7 @@ def bench_act(args):
             "buffer_sets": nset,
             "group_size": G,
             "algorithmic_bytes_per_step": nbytes,
+            "calls_per_event_pair": ACT_CALLS_PER_EVENT,
             "launch_ms_median": round(launch_sorted[len(launch_sorted) // 2], 5),
             "launch_ms_min": round(launch_sorted[0], 5),
             "copy_ceiling_GBps": round(ceiling, 1),

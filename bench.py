@@ -242,14 +242,18 @@ def cpu_baseline(specs, G, hp, sample_params, min_seconds=8.0):
         for it in sl:
             _oracle_step(it, 2, G, hp)
         dts = time.perf_counter() - t0
+        n_full = sum(sp.numel for sp in wspecs)
         single[name] = {"value": round(ns / dts / 1e6, 3), "unit": "Mparam/s",
                         "sample": f"{ns} params (first <=2M elements of the first {len(sl)} "
-                                  f"tensors), step 2 after an untimed step 1, {dts:.2f} s wall"}
+                                  f"tensors), step 2 after an untimed step 1, {dts:.2f} s wall",
+                        "full_step_s_extrapolated": round(n_full * dts / ns, 1)}
         del sl
-    return {"value": steps * n_total / dt / 1e9, "unit": "Gparam/s", "cores": threads,
+    rate = steps * n_total / dt
+    return {"value": rate / 1e9, "unit": "Gparam/s", "cores": threads,
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n_total} params: first <=2M elements of the first tensors, "
                       f"{steps} whole steps after one untimed step, {dt:.2f} s wall",
+            "full_step_s_extrapolated": round(sum(sp.numel for sp in specs) / rate, 1),
             "single_core": dict(single, cores=1)}
 
 
@@ -281,7 +285,7 @@ def cpu_baseline_act(rows, cols, G, transpose, min_seconds=10.0):
             if dt >= min_seconds:
                 break
     return {"value": passes * rows * cols / dt / 1e9, "unit": "Gelem/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"the whole {rows}x{cols} matrix, {passes} passes after an untimed one, "
                       f"{dt:.2f} s wall"}
 
@@ -522,6 +526,7 @@ def cpu_baseline_gemm(a, b, sa, sb, G, min_seconds=10.0):
                 break
     flops = passes * 2.0 * sum(x.shape[0] for x in sel) * N * K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{sum(x.shape[0] for x in sel)} of {M} rows x {N} x {K} (exact int64 "
                       f"sums), {passes} passes after an untimed one, {dt:.2f} s wall"}
 
@@ -683,7 +688,7 @@ def cpu_baseline_codec(G, sample, min_seconds=10.0):
             if dt >= min_seconds:
                 break
     return {"value": passes * sample / dt / 1e9, "unit": "Gelem/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{sample} N(0, 1e-3) FP32 values, {passes} round trips "
                       f"(expand-quantize, then dequantize-expand), {dt:.2f} s wall"}
 

@@ -1,7 +1,9 @@
 """GPU parity of the per-group activation quantizer (coat_fp8_quantize_act)
-against the oracle: bit-exact codes, scales and transposed codes.  Both sides
-take every rounding decision in FP32 (r = 448 / max, x * r, max / 448), so no
-tolerance applies.  Cases: every group size over tile-aligned and ragged
+against the oracle: bit-exact codes, scales and transposed codes.  The oracle
+codes the exact quotient 448 x / max and stores max / 448 rounded once to
+FP32; the kernel's FP32 quotient is exact at midpoints, and for BF16 inputs
+the exact quotient is either a midpoint or far (relative 2^-13 and more) from
+every midpoint, so no tolerance applies.  Cases: every group size over tile-aligned and ragged
 shapes (rows not a multiple of 64 or 16, cols not a multiple of 128), the
 stress recipe (zero, single-nonzero, subnormal, tiny, huge, tie, -0.0 and
 wide-range groups), the variant without the transpose, the full 8192 x 11008

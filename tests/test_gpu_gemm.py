@@ -6,9 +6,11 @@ Exact inputs (small-integer E4M3 codes, power-of-two scales): every partial
 sum is an integer below 2^24, so the FP32 accumulation is exact in any order
 and C and the scales must equal the oracle's bit for bit.  The oracle codes
 each value as the page's quantizer does, RNE of the exact quotient
-448 C / max; the kernel rounds C * fl(448 / max) in FP32, within 2^-23 of it.
-So at least 99.99% of codes must be identical, and every other code must be
-a neighbour of the oracle's across a midpoint that the exact quotient lies
+448 C / max.  The kernel divides fl(7/8 C) by max / 512 with one FMA
+refinement (exact at midpoints); that is the exact quotient whenever C has at
+most 21 significant bits, and within about 2^-23 of it otherwise.  So at
+least 99.99% of codes must be identical, and every other code must be a
+neighbour of the oracle's across a midpoint that the exact quotient lies
 within 2^-21 (relative) of.
 
 Realistic inputs (per-tensor E4M3 activations with outlier channels and
@@ -193,9 +195,10 @@ def test_negative_scale_signed_zeros(G):
 @pytest.mark.parametrize("G", [16, 128])
 @pytest.mark.parametrize("shape", SCALE_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SCALE_SHAPES])
 def test_tiny_scale_product(G, shape):
-    """s = 2^-120: every group maximum lies below 2^-100, where 448 / max
-    leaves FP32's range; those groups are quantized from fl(c s) with the
-    2^64 pre-scale: scales and C bit for bit, codes by the near-tie rule."""
+    """s = 2^-120: every group maximum lies below 2^-100, where the kernel's
+    FP32 reciprocal of max / 512 would leave the normal range; those groups
+    are quantized from fl(c s) with the 2^64 pre-scale: scales and C bit for
+    bit, codes by the near-tie rule."""
     M, N, K = shape
     a, b, _, _ = inputs.fp8_operands(M, N, K, 5, DEV, "exact")
     sa = sb = 2.0 ** -60

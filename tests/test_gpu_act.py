@@ -209,3 +209,43 @@ def test_random_shapes_bit_exact(case):
     if not transpose:
         ref = (ref[0], ref[1], None)
     _assert_same(f"random {case}", gpu, ref)
+
+
+def test_graph_capture_replays_match_eager():
+    """Three quantizer calls captured in one HIP graph: a ragged matrix on
+    64-row tiles with and without the transpose, and a 4096 x 4096 matrix on
+    128-row tiles.  The graph is replayed three times, with the outputs reset
+    and eager work between replays; every replay's codes, scales and
+    transposed codes equal an eager call's bit for bit."""
+    coat = lib()
+    cases = [(300, 1152, 64, True), (300, 1152, 64, False), (4096, 4096, 128, True)]
+    xs = [inputs.activation(r, c, 31 + i, DEV, "llm", G) for i, (r, c, G, _) in enumerate(cases)]
+    eager, captured = [], []
+    for x, (r, c, G, tr) in zip(xs, cases):
+        e = _outputs(r, c, G, tr)
+        coat.quantize_act(x, *e, group_size=G)
+        eager.append(e)
+        captured.append(_outputs(r, c, G, tr))
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x, (r, c, G, tr), o in zip(xs, cases, captured):
+            coat.quantize_act(x, *o, group_size=G)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        for codes, scales, codes_t in captured:
+            codes.fill_(SENTINEL)
+            scales.fill_(float("nan"))
+            if codes_t is not None:
+                codes_t.fill_(SENTINEL)
+        scratch = torch.randn(1 << 16, device=DEV).sum()      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for case, e, g in zip(cases, eager, captured):
+            assert torch.equal(g[0], e[0]), f"replay {replay} {case}: codes"
+            assert torch.equal(g[1].view(torch.int32), e[1].view(torch.int32)), \
+                f"replay {replay} {case}: scales"
+            if e[2] is not None:
+                assert torch.equal(g[2], e[2]), f"replay {replay} {case}: transposed codes"
+        del scratch

@@ -206,3 +206,41 @@ def test_full_size_codec_sampled_groups():
           f"{rel.max(initial=0):.2e}", flush=True)
     del x, y, st
     torch.cuda.empty_cache()
+
+
+def test_graph_capture_replays_match_eager():
+    """Expand-quantize and then dequantize-expand of the same state (n with
+    a partial last group), captured in one HIP graph and replayed three times
+    with the outputs reset and eager work between replays: every replay's
+    codes, scale, k and FP32 output equal an eager call's bit for bit."""
+    coat = lib()
+    G, n = 32, 70000 + 3
+    rng = np.random.default_rng(404)
+    x = torch.from_numpy(_random_groups(rng, n, G, [0.0, 0.5, 4, 10, 20, 40])).to(DEV)
+    st_e = coat.QuantState.zeros(n, G, DEV)
+    y_e = torch.empty(n, dtype=torch.float32, device=DEV)
+    coat.expand_quantize(x, st_e, G)
+    coat.dequantize_expand(st_e, y_e, G)
+    st_g = coat.QuantState.zeros(n, G, DEV)
+    y_g = torch.empty(n, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        coat.expand_quantize(x, st_g, G)
+        coat.dequantize_expand(st_g, y_g, G)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        st_g.codes.fill_(0xA5)
+        st_g.scale.fill_(float("nan"))
+        st_g.k.fill_(float("nan"))
+        y_g.fill_(float("nan"))
+        scratch = torch.randn(1 << 16, device=DEV).sum()      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st_g.codes, st_e.codes), f"replay {replay}: codes"
+        assert torch.equal(st_g.scale.view(torch.int32), st_e.scale.view(torch.int32)), \
+            f"replay {replay}: scale"
+        assert torch.equal(st_g.k.view(torch.int32), st_e.k.view(torch.int32)), f"replay {replay}: k"
+        assert torch.equal(y_g.view(torch.int32), y_e.view(torch.int32)), f"replay {replay}: output"
+        del scratch

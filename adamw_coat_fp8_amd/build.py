@@ -1,6 +1,7 @@
 """Build libcoat_fp8.so (gfx950 HIP kernels + C ABI) in the package folder,
-and libcoat_bench.so, the benchmark's measurement kernel (the math-free copy
-of the step's traffic; not part of the library's C ABI).
+and libcoat_bench.so, the benchmark's measurement kernels (the math-free copy
+of the step's traffic and plain read-only and write-only streams; not part
+of the library's C ABI).
 
 hipcc cross-compiles for gfx950 without a GPU.  Packed FP32 instructions are
 disabled (-packed-fp32-ops): the kernels are written as scalar float code.
@@ -13,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", f) for f in ("coat_fp8.hip", "coat_act.hip", "coat_gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libcoat_fp8.so")
-BENCH_SOURCES = [os.path.join(HERE, "csrc", "coat_mix_ceiling.hip")]
+BENCH_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("coat_mix_ceiling.hip", "coat_stream_ceiling.hip")]
 BENCH_LIB = os.path.join(HERE, "libcoat_bench.so")
 ARCH = "gfx950"
 

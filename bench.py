@@ -17,7 +17,9 @@ Prints ONE JSON line: Gparam/s over the timed steps, plus the step kernel's
 roofline position (algorithmic bytes per launch / average launch duration,
 HIP events on the launch stream), the rate of a math-free kernel that moves
 exactly the step's traffic with its lane layout (libcoat_bench.so: the
-streaming ceiling of this read/write mix, timed on the same shard), the
+streaming ceiling of this read/write mix, timed on the same shard), plain
+read-only and write-only streams on the same shard (after the steps; the
+write stream overwrites the gradient buffer), the
 stress recipe at G = 128, 64, 32 and 16 (one shard each, alternating timed
 rounds in this process), and the CPU oracle timed on bounded samples on the
 host cores (all threads, and one thread on the single 1024 x 1024 tensor and
@@ -845,6 +847,64 @@ def mix_ceiling(shard, reps: int = 10):
     return nbytes / (ms * 1e-3) / 1e9, ms, nbytes
 
 
+def separate_streams_gbps(G: int, read_gbps: float, write_gbps: float) -> float:
+    """Rate of the step's traffic (8 + 16/G bytes read and 6 + 16/G written
+    per parameter) if the reads moved at `read_gbps` and the writes at
+    `write_gbps` one after the other, with no read/write mixing."""
+    rd, wr = 8 + 16 / G, 6 + 16 / G
+    return (rd + wr) / (rd / read_gbps + wr / write_gbps)
+
+
+def stream_ceilings(shard, reps: int = 10):
+    """Plain read-only and write-only streams (libcoat_bench.so) on the same
+    shard: the read stream over its FP32 weights, the write stream over its
+    BF16 gradient buffer, which it overwrites with zeros (call it only once
+    the gradients are no longer needed).  Returns GB/s for each: bytes per
+    launch over the average launch time of `reps` launches (HIP events on
+    the launch stream), after two untimed launches."""
+    import ctypes
+    import torch
+
+    lib = ctypes.CDLL(BENCH_LIB)
+    vp = ctypes.c_void_p
+    lib.coat_bench_read_stream.restype = ctypes.c_int
+    lib.coat_bench_read_stream.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, vp, vp]
+    lib.coat_bench_write_stream.restype = ctypes.c_int
+    lib.coat_bench_write_stream.argtypes = [vp, ctypes.c_int64, ctypes.c_uint32, vp]
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(256, dtype=torch.int32, device=shard.w.device)
+    rbytes = shard.w.numel() * 4 // 16 * 16
+    wbytes = shard.grad.numel() * 2 // 16 * 16
+
+    def read():
+        rc = lib.coat_bench_read_stream(shard.w.data_ptr(), rbytes, 0x9E3779B9,
+                                        sink.data_ptr(), stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"coat_bench_read_stream returned {rc}")
+
+    def write():
+        rc = lib.coat_bench_write_stream(shard.grad.data_ptr(), wbytes, 0, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"coat_bench_write_stream returned {rc}")
+
+    def rate(fn, nbytes):
+        fn()
+        fn()
+        ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+        return nbytes / (ms * 1e-3) / 1e9
+
+    out = rate(read, rbytes), rate(write, wbytes)
+    del sink
+    return out
+
+
 def time_shard_steps(shard, t, hp, stream, steps, per_launch=False):
     """`steps` timed steps of a warm shard (HIP events around each step, or
     around each launch): returns (per-step ms list, per-launch ms list)."""
@@ -975,10 +1035,14 @@ def bench_step(args):
         inputs.fill_gradients(shard, 1, stds)
         gbps, ms, nbytes = mix_ceiling(shard, max(args.steps, 2))
         print(f"[bench] math-free copy: avg launch {ms:.4f} ms", file=sys.stderr, flush=True)
+        read_gbps, write_gbps = stream_ceilings(shard, max(args.steps, 2))
+        print(f"[bench] read-only stream {read_gbps:.1f} GB/s, write-only stream "
+              f"{write_gbps:.1f} GB/s", file=sys.stderr, flush=True)
         if args.copy_probe:
             copy_probe()
         print(json.dumps({"mix_ceiling_GBps": round(gbps, 1), "avg_launch_ms": round(ms, 4),
-                          "bytes_per_launch": nbytes}), flush=True)
+                          "bytes_per_launch": nbytes, "read_stream_GBps": round(read_gbps, 1),
+                          "write_stream_GBps": round(write_gbps, 1)}), flush=True)
         return
     call_lists = shard.calls
     call_bytes = [sum(algorithmic_bytes(numels[i], G) for i in c) for c in shard.call_indices]
@@ -1020,6 +1084,9 @@ def bench_step(args):
     ceiling_gbps, ceiling_ms, _ = mix_ceiling(shard)
     print(f"[bench] math-free copy of the step's traffic: {ceiling_gbps:.1f} GB/s "
           f"({ceiling_ms:.3f} ms per launch over the whole shard)", file=sys.stderr, flush=True)
+    read_gbps, write_gbps = stream_ceilings(shard)     # overwrites the gradients: steps are done
+    print(f"[bench] plain streams on the same shard: read-only {read_gbps:.1f} GB/s, "
+          f"write-only {write_gbps:.1f} GB/s", file=sys.stderr, flush=True)
     if args.copy_probe:
         copy_probe()
 
@@ -1081,6 +1148,11 @@ def bench_step(args):
             "step_ms_min": round(step_ms[0], 4),
             "mix_ceiling_GBps": round(ceiling_gbps, 1),
             "frac_of_mix_ceiling": round(achieved / ceiling_gbps, 4),
+            "read_only_stream_GBps": round(read_gbps, 1),
+            "write_only_stream_GBps": round(write_gbps, 1),
+            # the step's bytes if its reads ran at the read-only rate and its
+            # writes at the write-only rate, one after the other (no mixing)
+            "separate_streams_bound_GBps": round(separate_streams_gbps(G, read_gbps, write_gbps), 1),
             "copy_ceiling_GBps": round(ceiling, 1),
             "kernel_frac_of_copy_ceiling": round(achieved / ceiling, 4),
         },

@@ -154,3 +154,18 @@ def test_shard_over_another_shards_storage():
         assert sh.slot(i).w.numel() == n
     with pytest.raises(ValueError):
         FP8AdamWShard(numels, group_size=16, device="cpu", storage=sh)
+
+
+def test_bench_separate_streams_bound():
+    """The no-mixing bound of the step's traffic: equal read and write rates
+    give that rate; otherwise the byte-weighted harmonic mean of the two, with
+    8 + 16/G bytes read and 6 + 16/G written per parameter."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.separate_streams_gbps(128, 5000.0, 5000.0) == pytest.approx(5000.0)
+    rd, wr = 8.125, 6.125
+    want = (rd + wr) / (rd / 6500.0 + wr / 5900.0)
+    assert bench.separate_streams_gbps(128, 6500.0, 5900.0) == pytest.approx(want)
+    assert 5900.0 < want < 6500.0
+    # smaller groups move more per-group bytes both ways
+    assert bench.separate_streams_gbps(16, 6500.0, 5900.0) != pytest.approx(want)

@@ -85,6 +85,15 @@ __device__ __forceinline__ float scale_acc(float acc, float s) {
   return acc * s;
 }
 
+// The output rows leave as 16-byte stores with the nontemporal hint: the
+// kernel never reads them back (measured: 0.4-1.9% faster calls across four
+// Llama-2-7B shapes, outputs unchanged).
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_out16(void* p, uint4 v) {
+  const u32x4v w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4v*>(p));
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
@@ -357,7 +366,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
       const uint8_t* rtile = lds_part_rt(row >> 6);
       const uint4 v = *reinterpret_cast<const uint4*>(rtile + bf16_off(row, 16 * c));
       if (m0 + row < p.M && 8 * c < n_valid)
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(p.c_bf16 + (m0 + row) * p.N + n0) + 16 * c) = v;
+        store_out16(reinterpret_cast<uint8_t*>(p.c_bf16 + (m0 + row) * p.N + n0) + 16 * c, v);
     }
   } else {
     constexpr int kGW = 128 / G;   // groups per row in the wave's 128 columns
@@ -483,7 +492,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
       uint4 v = *reinterpret_cast<const uint4*>(rtile + (row & 127) * 256 + ((c ^ (row & 15)) << 4));
       if ((row >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
       if (m0 + row < p.M && 16 * c < n_valid)
-        *reinterpret_cast<uint4*>(p.codes + (m0 + row) * p.N + n0 + 16 * c) = v;
+        store_out16(p.codes + (m0 + row) * p.N + n0 + 16 * c, v);
     }
   }
 }

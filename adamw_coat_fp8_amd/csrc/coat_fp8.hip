@@ -524,12 +524,21 @@ __device__ __forceinline__ void load_lane(const TensorDesc& T, const LaneMap<G, 
   }
 }
 
-template <int G, bool kFull, int E = kElemsPerLane>
+// kNT: the nontemporal hint on the full-tile stores.  The stand-alone codec
+// takes it (measured on MI355X over an 8 GB vector: expand-quantize 3.3%,
+// dequantize-expand 1.2% faster, outputs unchanged); the step does not, as
+// it gains nothing there.
+template <int G, bool kFull, int E = kElemsPerLane, bool kNT = false>
 __device__ __forceinline__ void store_codes(uint8_t* base, const LaneMap<G, E>& map, int64_t n,
                                             const uint32_t (&c)[E / 4]) {
   if constexpr (kFull) {
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q) *reinterpret_cast<uint32_t*>(base + map.run(q)) = c[q];
+    for (int q = 0; q < E / 4; ++q) {
+      if constexpr (kNT)
+        __builtin_nontemporal_store(c[q], reinterpret_cast<uint32_t*>(base + map.run(q)));
+      else
+        *reinterpret_cast<uint32_t*>(base + map.run(q)) = c[q];
+    }
   } else {
     for (int j = 0; j < E; ++j) {
       const int64_t e = map.elem(j);
@@ -538,14 +547,22 @@ __device__ __forceinline__ void store_codes(uint8_t* base, const LaneMap<G, E>& 
   }
 }
 
-template <int G, bool kFull, int E = kElemsPerLane, int B = default_block(G)>
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int G, bool kFull, int E = kElemsPerLane, int B = default_block(G), bool kNT = false>
 __device__ __forceinline__ void store_floats(float* base, const LaneMap<G, E, B>& map, int64_t n,
                                              const float (&x)[E]) {
   if constexpr (kFull) {
 #pragma unroll
-    for (int q = 0; q < E / 4; ++q)
-      *reinterpret_cast<float4*>(base + map.run(q)) =
-          make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+    for (int q = 0; q < E / 4; ++q) {
+      if constexpr (kNT) {
+        const f32x4v v = {x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(base + map.run(q)));
+      } else {
+        *reinterpret_cast<float4*>(base + map.run(q)) =
+            make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+      }
+    }
   } else {
     for (int j = 0; j < E; ++j) {
       const int64_t e = map.elem(j);
@@ -771,7 +788,7 @@ __device__ __forceinline__ void quantize_lane(const CodecParams& p, int64_t tile
     for (int r = 0; r < 4; ++r) a[r] = copysignf(quant_mag(x[4 * q + r], qc), x[4 * q + r]);
     o[q] = pack4(a[0], a[1], a[2], a[3]);
   }
-  store_codes<G, kFull>(p.codes, map, p.n, o);
+  store_codes<G, kFull, kElemsPerLane, true>(p.codes, map, p.n, o);
   if ((lane % kLanesPerGroup) == 0 && grp_ok) {
     p.scale[grp] = qc.scale;
     p.k[grp] = qc.k;
@@ -810,7 +827,7 @@ __device__ __forceinline__ void dequantize_lane(const CodecParams& p, int64_t ti
     const float2 e = tab[(c[j >> 2] >> (8 * (j & 3))) & 0xFF];
     x[j] = dequant_mag(e.x, d) * e.y;
   }
-  store_floats<G, kFull, kElemsPerLane, G>(p.xo, map, p.n, x);
+  store_floats<G, kFull, kElemsPerLane, G, true>(p.xo, map, p.n, x);
 }
 
 // Same split as the step: kTail = false walks the full tiles, kTail = true

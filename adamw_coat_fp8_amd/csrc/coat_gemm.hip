@@ -25,10 +25,12 @@
 // Quantization.  With c the FP32 accumulator and C = fl(c s), the group
 // maximum of |C| is fl(max |c| * |s|) exactly (rounding is monotone) and the
 // stored scale is that maximum / 448.  Each code is the E4M3 rounding of the
-// quotient 448 C / max formed by group_quot (coat_common.h): exact at ties,
-// and for C of at most 21 significant bits exact everywhere.  Groups whose
-// maximum lies below 2^-100 take group_quot's 2^64 pre-scale in a second,
-// rarely taken pass.
+// quotient 448 C / max formed by group_quot (coat_common.h) from the hardware
+// reciprocal of max / 512 (within one ulp): the FMA refinement lands exactly
+// on a midpoint whenever the quotient is one, so ties are decided exactly,
+// and elsewhere the refined quotient lies within about 2^-22 of the exact
+// one.  Groups whose maximum lies below 2^-100 take group_quot's 2^64
+// pre-scale in a second, rarely taken pass.
 
 #include <hip/hip_runtime.h>
 
@@ -408,7 +410,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
           amax[i][g] = fmaxf(fmaxf(amax[i][g], fabsf(acc[i][j][4 * q + 2])), fabsf(acc[i][j][4 * q + 3]));
         }
     // Per group: the stored scale max / 448 and the divisor b = max / 512 with
-    // its reciprocal r, for group_quot on C = fl(c s) (a = C * 7/8, q = a / b).
+    // its reciprocal r (v_rcp_f32; the refinement in group_quot keeps ties
+    // exact), for group_quot on C = fl(c s) (a = C * 7/8, q = a / b).  With
+    // G = 16 a lane forms 16 of these per tile: the hardware reciprocal cut
+    // the call by 1-2% there against a rounded division.
     // Groups whose max lies below 2^-100 (or past FP32's range) need the
     // 2^64 pre-scale; they get b = r = 0 here (all codes 0) and are redone
     // below.
@@ -421,7 +426,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, const int64_t bid
         amax[i][g] = scale_acc(pair_max(amax[i][g]), s_abs);
         const bool fast = amax[i][g] >= 0x1p-100f && amax[i][g] <= 0x1.fffffep127f;
         qb[i][g] = fast ? amax[i][g] * 0x1p-9f : 0.0f;
-        qr[i][g] = fast ? 1.0f / qb[i][g] : 0.0f;
+        qr[i][g] = fast ? __builtin_amdgcn_rcpf(qb[i][g]) : 0.0f;
         slow |= !fast && amax[i][g] > 0.0f;
       }
     uint32_t word[kI][4][4];

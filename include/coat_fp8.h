@@ -185,10 +185,10 @@ coat_status_t coat_fp8_quantize_act(const uint16_t* x, int64_t rows,
  *   matrix cores as c = A B^T, then each 1xG group of a row of C is
  *   quantized from C = fl(c s): S = max|C| / 448 (max|C| = fl(max|c| * |s|)
  *   exactly, rounding being monotone) and each code the E4M3 rounding of
- *   448 C / max|C|, formed as in coat_fp8_quantize_act (exact at every E4M3
- *   value and midpoint; exact everywhere when C has at most 21 significant
- *   bits; otherwise a code can differ only for a quotient within about
- *   2^-21 relative of a midpoint).  -0 -> 0x00, an all-zero group -> S = 0
+ *   448 C / max|C|, formed as in coat_fp8_quantize_act but from the
+ *   hardware reciprocal of max/512 (exact at every E4M3 value and midpoint;
+ *   elsewhere a code can differ from the exact quotient's only for a
+ *   quotient within about 2^-21 relative of a midpoint).  -0 -> 0x00, an all-zero group -> S = 0
  *   and codes 0; groups whose max lies below 2^-100 take the 2^64 pre-scale.
  *   a        M x K E4M3 codes, row-major (read only).
  *   b        N x K E4M3 codes, row-major (read only): the weight of a linear

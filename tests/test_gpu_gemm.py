@@ -6,9 +6,9 @@ Exact inputs (small-integer E4M3 codes, power-of-two scales): every partial
 sum is an integer below 2^24, so the FP32 accumulation is exact in any order
 and C and the scales must equal the oracle's bit for bit.  The oracle codes
 each value as the page's quantizer does, RNE of the exact quotient
-448 C / max.  The kernel divides fl(7/8 C) by max / 512 with one FMA
-refinement (exact at midpoints); that is the exact quotient whenever C has at
-most 21 significant bits, and within about 2^-23 of it otherwise.  So at
+448 C / max.  The kernel divides fl(7/8 C) by max / 512 through the
+hardware reciprocal and one FMA refinement: exact when the quotient is a
+midpoint, and within about 2^-22 of the exact quotient otherwise.  So at
 least 99.99% of codes must be identical, and every other code must be a
 neighbour of the oracle's across a midpoint that the exact quotient lies
 within 2^-21 (relative) of.

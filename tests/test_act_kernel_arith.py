@@ -7,7 +7,9 @@ the E4M3 rounding of q1 must equal the definition's rounding of the exact
 quotient 448 x / max (e4m3_exact) on random BF16 groups, on groups built from
 exact ties with maxima that are not powers of two, and on tiny and huge
 groups; -0.0 must come out as +0 (code 0x00) and a negative quotient that
-underflows as -0 (0x80)."""
+underflows as -0 (0x80).  The linear layer forms r with the hardware
+reciprocal (within one ulp): with r one or two ulps off, exact ties of FP32
+quotients must still go to the even code, and BF16 codes must not change."""
 import math
 from fractions import Fraction
 
@@ -63,14 +65,27 @@ def _fma(x, y, z):
     return _round(p + z[0], both_neg_zero)
 
 
-def kernel_code(x: float, amax: float) -> int:
-    """E4M3 code of x as the kernel computes it, every FP32 step exact."""
+def _ulp(v: Fraction) -> Fraction:
+    """Spacing of FP32 values at the normal magnitude v."""
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    return Fraction(2) ** (e - 23)
+
+
+def kernel_code(x: float, amax: float, r_ulps: int = 0, exact_a: bool = True) -> int:
+    """E4M3 code of x as the kernel computes it, every FP32 step exact.
+    r_ulps moves the reciprocal r = fl(1/b) by that many ulps: the hardware
+    reciprocal that the linear layer uses is within one ulp of 1/b."""
     pre = Fraction(2) ** 64 if amax < 2.0 ** -100 else Fraction(1)
     c = (Fraction(7, 8) * pre, False)
     b = (f32(Fraction(amax) * pre / 512), False)
-    r = (f32(1 / b[0]), False)
-    a = _mul(_val(x), c)                  # exact for BF16 x (asserted below)
-    assert a[0] == Fraction(x) * c[0]
+    r0 = f32(1 / b[0])
+    r = (r0 + r_ulps * _ulp(r0), False)
+    a = _mul(_val(x), c)
+    if exact_a:                           # exact for BF16 x
+        assert a[0] == Fraction(x) * c[0]
     q0 = _mul(a, r)
     e = _fma((-q0[0], not q0[1]), b, a)
     q1 = _fma(e, r, q0)
@@ -137,3 +152,43 @@ def test_signed_zero_helpers_follow_ieee():
                 want = x * y + z
                 got = _fma(_val(x), _val(y), _val(z))
                 assert got[0] == Fraction(want) and got[1] == (math.copysign(1.0, want) < 0), (x, y, z)
+
+
+
+def test_ties_stay_exact_with_an_approximate_reciprocal():
+    """The refinement q1 = fma(fma(-q0, b, a), r, q0) lands exactly on a
+    midpoint M whenever a / b = M, for r up to two ulps off 1/b: q0 is then a
+    few ulps from M, the residual b (M - q0) is exact, and the correction's
+    error is far below half an ulp.  FP32 values C with 21-24 significant
+    bits over maxima that are not powers of two, ties to the even code."""
+    n = 0
+    # maxima 7 m 2^e with m odd and up to 16 bits make both C = M max / 448
+    # and 7/8 C exact FP32 values for every midpoint M
+    for amax in (3.25, 98.0 + 2.0 ** -17, 25.5 * (1 + 2.0 ** -21), 7.0 * (1 - 2.0 ** -22),
+                 7.0 * 40961 * 2.0 ** -10, 7.0 * 65533 * 2.0 ** -20, 7.0 * 52429 * 2.0 ** 5,
+                 7.0 * 3 * 2.0 ** -30, 7.0 * 12345 * 2.0 ** 40):
+        amax = float(np.float32(amax))
+        for lo, hi in zip(E4M3_VALUES, E4M3_VALUES[1:]):
+            x = (lo + hi) / 2 * Fraction(amax) / 448        # a / b is exactly the midpoint
+            if f32(x) != x or f32(x * Fraction(7, 8)) != x * Fraction(7, 8):
+                continue
+            n += 1
+            for k in (-2, -1, 1, 2):
+                for v in (float(x), -float(x)):
+                    assert kernel_code(v, amax, k, exact_a=False) == exact_code(v, amax), (v, amax, k)
+    assert n >= 40
+
+
+def test_bf16_codes_keep_with_an_approximate_reciprocal():
+    """For BF16 groups the codes do not depend on the reciprocal's last bits:
+    a BF16 quotient that is not a midpoint lies at least 2^-12.8 (relative)
+    from every midpoint."""
+    rng = np.random.default_rng(5)
+    for scale in (1.0, 3e-3, 2.0 ** -110):
+        x = _bf16(rng.standard_normal(512) * scale).reshape(4, 128)
+        for grp in x:
+            amax = float(np.abs(grp).max())
+            for v in grp[:64]:
+                want = exact_code(float(v), amax)
+                for k in (-1, 1):
+                    assert kernel_code(float(v), amax, k) == want, (v, amax, k)

@@ -339,6 +339,23 @@ def test_full_size_sampled_rows():
     _interval_check("full llm", a, b, sa, sb, G, (gc[sel], gs[sel], None), rows=sel)
 
 
+@pytest.mark.parametrize("G", [16, 32, 64])
+def test_full_size_other_group_sizes(G):
+    """8192 x 11008 x 4096 at the other group sizes the benchmark reports, in
+    its launch: exact inputs on six sampled rows (the first and last among
+    them), scales bit for bit and codes by the near-tie rule."""
+    M, N, K = 8192, 11008, 4096
+    rng = np.random.default_rng(G)
+    a, b, sa, sb = inputs.fp8_operands(M, N, K, 20 + G, DEV, "exact")
+    print(f"[gemm] full size G={G}", flush=True)
+    gc, gs, _ = _run(a, b, sa, sb, G, want_c=False)
+    sel = np.sort(rng.choice(M, 6, replace=False))
+    sel[0], sel[-1] = 0, M - 1
+    codes, scales, _, c32 = oracle.gemm_fp8_group_quant(a.cpu().numpy()[sel], b.cpu().numpy(),
+                                                        sa, sb, G, want_c=True)
+    _assert_bit_exact(f"full exact G={G}", (gc[sel], gs[sel], None), (codes, scales, c32), G)
+
+
 # the other Llama-2-7B linear-layer shapes the benchmark is run at: FFN down,
 # fused gate + up, fused QKV, attention output, and a single round of tiles
 LLAMA_SHAPES = [(8192, 4096, 11008), (8192, 22016, 4096), (8192, 12288, 4096),

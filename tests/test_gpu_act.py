@@ -127,13 +127,15 @@ def test_tile_height_switch_bit_exact(shape):
     _assert_same(f"tile switch {rows}x{cols}", _gpu(x, G), _oracle(x, G))
 
 
-def test_full_size_sampled_rows():
-    """8192 x 11008 (4 sequences of 2048 tokens, FFN width 11008), G = 128, in
-    the launch the benchmark times.  Oracle on 48 sampled rows (each row is
-    independent), and codes_t == codes^T checked over every element on the
-    device."""
+@pytest.mark.parametrize("G", [128, 64, 32, 16])
+def test_full_size_sampled_rows(G):
+    """8192 x 11008 (4 sequences of 2048 tokens, FFN width 11008) at each
+    group size, in the launch the benchmark times.  Oracle on 48 sampled rows
+    (each row is independent), and codes_t == codes^T checked over every
+    element on the device."""
     coat = lib()
-    rows, cols, G = 8192, 11008, 128
+    rows, cols = 8192, 11008
+    print(f"[act] full size G={G}", flush=True)
     x = inputs.activation(rows, cols, 0, DEV, "llm", G)
     codes, scales, codes_t = _outputs(rows, cols, G)
     coat.quantize_act(x, codes, scales, codes_t, group_size=G)

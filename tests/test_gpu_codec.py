@@ -158,21 +158,21 @@ def test_expand_quantize_matches_oracle(G, n):
     assert np.all(gk[~nz] == 1.0)
 
 
-def test_full_size_codec_sampled_groups():
+@pytest.mark.parametrize("G", [128, 32])
+def test_full_size_codec_sampled_groups(G):
     """Both codec entry points at the benchmark's launch: one call each over a
-    Llama-2-7B-sized FP32 first moment (6,738,415,616 values, G = 128, the
-    benchmark's input recipe).  On 1,500 sampled groups (the first, the one
+    Llama-2-7B-sized FP32 first moment (6,738,415,616 values, the benchmark's
+    input recipe, at G = 128 and at G = 32, the other group size measured).  On 1,500 sampled groups (the first, the one
     holding element 2^31, the last, and random ones): expand-quantize against
     the oracle's (scale exact, k within 1e-5, codes by the parity rules), and
     dequantize-expand of the GPU's own state against the oracle's
     dequantization of it (within the relative error bound)."""
     from adamw_coat_fp8_amd import inputs
     coat = lib()
-    G = 128
     numels = [s.numel for s in inputs.workload_specs("llama2_7b")]
     n = sum(numels)
     ng = n // G
-    print(f"[codec] full size: {n} values", flush=True)
+    print(f"[codec] full size: {n} values, G={G}", flush=True)
     x = inputs.fill_moment_like(torch.empty(n, dtype=torch.float32, device=DEV), numels,
                                 inputs.grad_stds(len(numels)))
     st = coat.QuantState.zeros(n, G, DEV)
